@@ -1,0 +1,212 @@
+/*
+ * pagedkv.h - C ABI of the MI355X (gfx950) paged-KV attention step of one
+ * transformer layer.
+ *
+ * The step follows the Req/Batch model described in "mini-sglang learning
+ * notes" (doc-mini-sglang-learn: the Req, Batch, KV-pool, page-table,
+ * store_kv and dummy-page passages) and "mini-sglang architecture deep dive"
+ * (tinymind.me) sections 5.1-5.3 and 6.2:
+ *
+ *   build_attn_metadata  page-table write for the batch's new tokens, out_loc,
+ *                        positions, running totals, and the attention plan
+ *   kv_store             scatter of the new K/V rows to their out_loc rows
+ *   paged_decode_attn    split-K decode attention (one new token per request)
+ *   paged_extend_attn    chunked-prefill attention on a cached prefix
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer inside the structs and every data argument is a DEVICE
+ *     pointer unless marked "host".  The structs themselves are read on the
+ *     host during the call and may be freed when it returns.
+ *   - The caller owns every buffer.  The library never allocates, frees or
+ *     synchronises; it only enqueues kernels on `stream` (a hipStream_t,
+ *     passed as void*; NULL means the legacy default stream).  All calls are
+ *     asynchronous, stateless and reentrant, so they can be captured in a
+ *     HIP graph when the buffers keep fixed addresses.
+ *   - Return codes are checked on the host BEFORE any launch: on a non-zero
+ *     return nothing was enqueued (except PKV_ERR_HIP, which reports a
+ *     launch failure).  Values that live on the device (lengths, table
+ *     indices, out_loc, page-table entries) cannot be checked on the host;
+ *     kernels check each one before using it as an address, skip the
+ *     offending request / token / key, and OR a PKV_STATUS_* bit into the
+ *     caller's `status` word (if non-NULL).  A bad device value therefore
+ *     never causes an out-of-bounds access.
+ *   - bf16 is IEEE bfloat16; outputs are rounded from fp32 to nearest even.
+ *   - head_dim must be 128; query heads per KV head (Hq / Hkv) must be 1..16.
+ *     Consecutive query heads share a KV head: query head h reads KV head
+ *     h / (Hq / Hkv).
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes (host side) ------------------------------------------ */
+#define PKV_OK                    0
+#define PKV_ERR_INVALID_ARGUMENT  1  /* null pointer, negative size, bad stride or shape relation */
+#define PKV_ERR_UNSUPPORTED       2  /* head_dim != 128, Hq/Hkv outside 1..16, page_size not a power of two <= 64 */
+#define PKV_ERR_WORKSPACE         3  /* plan or workspace smaller than the size query returns */
+#define PKV_ERR_HIP               4  /* a kernel launch failed; see pkv_last_hip_error() */
+
+/* ---- device status bits (sticky; OR-ed into *status by kernels) ---------- */
+#define PKV_STATUS_BAD_OUT_LOC    0x01  /* out_loc[t] outside [0, num_rows): token skipped by kv_store */
+#define PKV_STATUS_BAD_LENGTHS    0x02  /* not 0 <= cached_len <= device_len <= W: request skipped */
+#define PKV_STATUS_BAD_TABLE_IDX  0x04  /* table_idx outside [0, R): request skipped */
+#define PKV_STATUS_BAD_PAGE_ROW   0x08  /* a page-table entry or new row outside the pool: key or token skipped */
+#define PKV_STATUS_BAD_DECODE     0x10  /* a request below num_decode whose extend_len != 1: skipped */
+#define PKV_STATUS_TOKEN_COUNT    0x20  /* sum of extend_len differs from num_tokens */
+#define PKV_STATUS_BAD_ALLOC      0x40  /* alloc_rows entry misaligned, outside the pool, or too few entries */
+
+/* ---- data structures ---------------------------------------------------- */
+
+/* One layer's KV pool: "each layer's K/V buffer is a (pages*page_size,
+ * kv_heads, head_dim) token-row array; a token's physical position is its row
+ * number" (learning notes, KV-pool passage; deep dive 6.2).
+ * Element (row r, KV head g, dim e) of K is at k + (r*row_stride + g*head_dim + e)
+ * bf16 elements; the same for V.  Page p owns rows [p*page_size, (p+1)*page_size). */
+typedef struct pkv_kv_pool {
+  void*   k;             /* bf16 K rows */
+  void*   v;             /* bf16 V rows */
+  int64_t num_rows;      /* rows in the pool; a multiple of page_size, < 2^31 */
+  int64_t row_stride;    /* bf16 elements from one row to the next; >= num_kv_heads*head_dim, multiple of 8 */
+  int32_t page_size;     /* 1, 2, 4, ..., 64 */
+  int32_t num_kv_heads;  /* Hkv */
+  int32_t head_dim;      /* d; must be 128 */
+  int32_t reserved;      /* must be 0 */
+} pkv_kv_pool;
+
+/* page_table (learning notes, page-table passage): one row per request slot
+ * (table_idx); column j holds the RAW physical pool row of logical token j;
+ * the width is aligned up to 32.  int32 [num_rows, width], row-major. */
+typedef struct pkv_page_table {
+  int32_t* data;
+  int32_t  num_rows;     /* R */
+  int32_t  width;        /* W; a positive multiple of 32 */
+} pkv_page_table;
+
+/* The batch (learning notes, Req and Batch passages).  For request i:
+ * cached_len = tokens already in the pool, device_len = tokens covered after
+ * this forward, extend_len = device_len - cached_len new tokens.  The new
+ * tokens of all requests are laid out in request order ("batch order"): q, o,
+ * k_new, v_new, out_loc and positions all have one row per new token in that
+ * order.  The first num_decode requests are decode requests (extend_len == 1);
+ * the rest are extend requests.  Padding requests (CUDA-graph-style batch
+ * filling) are ordinary decode requests with cached_len 0, device_len 1 and a
+ * table row whose entries all point at the dummy page. */
+typedef struct pkv_batch {
+  int32_t        num_reqs;    /* B >= 0 */
+  int32_t        num_decode;  /* 0 <= num_decode <= B */
+  int64_t        num_tokens;  /* T = sum of extend_len (host-known; sizes the per-token arrays) */
+  const int32_t* table_idx;   /* [B] page-table row of each request */
+  const int32_t* cached_len;  /* [B] */
+  const int32_t* device_len;  /* [B] */
+} pkv_batch;
+
+/* Per-batch metadata, written by build_attn_metadata into caller-owned
+ * buffers (fixed addresses allow graph replay) and read by the attention
+ * calls of every layer of that batch. */
+typedef struct pkv_attn_metadata {
+  int32_t* out_loc;       /* [T]   physical pool row of each new token */
+  int32_t* positions;     /* [T]   logical position (cached_len + offset) of each new token */
+  int32_t* qo_indptr;     /* [B+1] running total of extend_len, starting at 0 */
+  int32_t* kv_indptr;     /* [B+1] running total of device_len, starting at 0 */
+  int32_t* last_indices;  /* [B]   qo_indptr[i+1] - 1: row of each request's last new token */
+  void*    plan;          /* opaque work lists for the attention kernels */
+  size_t   plan_bytes;    /* >= pkv_plan_bytes(B, T, Hq, Hkv) */
+  int32_t* status;        /* [1] sticky PKV_STATUS_* bits, or NULL */
+} pkv_attn_metadata;
+
+/* ---- size queries (pure host functions) --------------------------------- */
+
+/* Bytes of pkv_attn_metadata.plan for batches of at most max_reqs requests and
+ * max_tokens new tokens with these head counts.  0 on invalid arguments. */
+size_t pkv_plan_bytes(int32_t max_reqs, int64_t max_tokens, int32_t num_qo_heads, int32_t num_kv_heads);
+
+/* Bytes of the workspace paged_decode_attn needs for at most max_reqs
+ * requests (the split-K partial results: fp32 accumulators plus running max
+ * and sum per split and query head).  0 on invalid arguments. */
+size_t paged_attn_workspace_bytes(int32_t max_reqs, int32_t num_qo_heads, int32_t head_dim);
+
+/* ---- entry points ------------------------------------------------------- */
+
+/* kv_store: K[out_loc[t]] = k_new[t] and V[out_loc[t]] = v_new[t] for
+ * t < num_tokens (learning notes, store_kv passage: each layer first scatters
+ * the batch's new K/V to the out_loc physical positions; the dummy page
+ * absorbs padding writes).
+ *   k_new, v_new : bf16 [num_tokens, Hkv, head_dim], contiguous
+ *   out_loc      : int32 [num_tokens]
+ * Tokens with the same target row (only padding tokens on the dummy page)
+ * race: that row ends up holding one of them, possibly mixed.  A token whose
+ * out_loc is outside the pool is skipped (PKV_STATUS_BAD_OUT_LOC).
+ * num_tokens == 0 is a no-op. */
+int kv_store(const pkv_kv_pool* pool, const void* k_new, const void* v_new, const int32_t* out_loc,
+             int64_t num_tokens, int32_t* status, void* stream);
+
+/* build_attn_metadata: for each request i and each new logical position
+ * j in [cached_len, device_len) (learning notes, page-table passage: page
+ * aligned allocation over [cached_len, device_len) from free_slots, written
+ * back with the raw physical rows):
+ *   - if j lies in the request's partially filled last cached page,
+ *       row = page_table[r, j - j % s] + j % s
+ *     otherwise it lies in the request's k-th new page and
+ *       row = alloc_rows[first new page of i + k] + j % s;
+ *   - page_table[table_idx[i], j] = row;  out_loc[t] = row;  positions[t] = j;
+ * and writes qo_indptr, kv_indptr, last_indices and the attention plan.
+ *   page_size  : s of the pool (a power of two <= 64)
+ *   num_pool_rows : rows of the pool (alloc rows + j % s must stay below it)
+ *   alloc_rows : int32 [num_alloc], the first pool row (a multiple of s) of
+ *                every newly allocated page, request by request; request i
+ *                takes ceil(device_len/s) - ceil(cached_len/s) pages.  With
+ *                s == 1 this is exactly out_loc.
+ *   num_qo_heads, num_kv_heads : head counts the plan is built for; the
+ *                attention calls must use the same ones.
+ * Requests with invalid lengths or table_idx are skipped (status bit set);
+ * entries outside [cached_len, device_len) of each row are left untouched. */
+int build_attn_metadata(const pkv_batch* batch, const pkv_page_table* page_table, int32_t page_size,
+                        int64_t num_pool_rows, const int32_t* alloc_rows, int64_t num_alloc,
+                        int32_t num_qo_heads, int32_t num_kv_heads, const pkv_attn_metadata* meta,
+                        void* stream);
+
+/* paged_decode_attn: for each decode request i < num_decode and query head h,
+ *   o[qo_indptr[i], h] = softmax(sm_scale * q[qo_indptr[i], h] . K[rows]^T) V[rows]
+ * over rows = page_table[table_idx[i], 0 .. device_len[i]) (the new row stored
+ * by kv_store included), gathered through the page table.  Split-K
+ * ("parallelise across KV", learning notes kernel passage; flash-decoding):
+ * each plan item covers a key range of one request, and a merge kernel
+ * combines the items' partial softmax states.
+ *   q, o       : bf16 [num_tokens, Hq, head_dim]; rows of extend requests untouched
+ *   workspace  : >= paged_attn_workspace_bytes(B, Hq, head_dim) bytes, 16-byte aligned
+ * Must follow build_attn_metadata (same batch, head counts) and kv_store on
+ * the same stream (or be ordered after them). */
+int paged_decode_attn(const pkv_kv_pool* pool, const pkv_page_table* page_table, const pkv_batch* batch,
+                      const pkv_attn_metadata* meta, const void* q, void* o, int32_t num_qo_heads,
+                      float sm_scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* paged_extend_attn: chunked prefill on a cached prefix (learning notes,
+ * Req and chunked-prefill passages; deep dive 5.2).  For each extend request
+ * i >= num_decode and its new token t (position p = cached_len + t) and query
+ * head h,
+ *   o[qo_indptr[i] + t, h] = softmax(sm_scale * q . K[rows 0..p]^T) V[rows 0..p]
+ * i.e. the whole cached prefix is visible and the new rows are causal.
+ * QK^T and PV run on bf16 MFMA with fp32 accumulation; the probabilities are
+ * rounded to bf16 before PV.
+ *   q, o : bf16 [num_tokens, Hq, head_dim]; rows of decode requests untouched
+ *   workspace : unused (may be NULL)
+ * Same ordering requirements as paged_decode_attn. */
+int paged_extend_attn(const pkv_kv_pool* pool, const pkv_page_table* page_table, const pkv_batch* batch,
+                      const pkv_attn_metadata* meta, const void* q, void* o, int32_t num_qo_heads,
+                      float sm_scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- diagnostics -------------------------------------------------------- */
+const char* pkv_error_string(int code);   /* static string, never NULL */
+int         pkv_last_hip_error(void);      /* hipError_t of the last PKV_ERR_HIP in this thread */
+int         pkv_version(void);             /* ABI version: 1 */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PAGEDKV_H */

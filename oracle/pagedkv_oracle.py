@@ -80,8 +80,22 @@ class KVPool:
         self._poison: set = set()
 
     def load(self, rows: Iterable[int], k_bits: np.ndarray, v_bits: np.ndarray) -> None:
+        """Bulk initial contents: rows[n] holds k_bits[n], v_bits[n] ([Hkv, d] each).
+        Rows are kept as read-only views of the given arrays."""
+        k_bits = np.asarray(k_bits, dtype=np.uint16).reshape(-1, self.num_kv_heads, self.head_dim)
+        v_bits = np.asarray(v_bits, dtype=np.uint16).reshape(-1, self.num_kv_heads, self.head_dim)
         for n, row in enumerate(rows):
-            self.write_row(int(row), k_bits[n], v_bits[n])
+            row = int(row)
+            if not (0 <= row < self.num_rows):
+                raise IndexError(f"pool row {row} outside [0, {self.num_rows})")
+            self._poison.discard(row)
+            if row in self._index:
+                self._k[self._index[row]] = k_bits[n]
+                self._v[self._index[row]] = v_bits[n]
+            else:
+                self._index[row] = len(self._k)
+                self._k.append(k_bits[n])
+                self._v.append(v_bits[n])
 
     def mark_poison(self, rows: Iterable[int]) -> None:
         self._poison.update(int(r) for r in rows)

@@ -1,0 +1,210 @@
+"""MI355X (gfx950) paged-KV attention step of one transformer layer.
+
+Thin Python binding over libpagedkv.so (see include/pagedkv.h): it checks
+tensor devices, dtypes and shapes, fills the C structs and calls the library
+on the current HIP stream.  Every step of the computation runs in the
+library's kernels; there is no other code path.
+
+Names follow the mini-sglang Req/Batch model: cached_len, device_len,
+extend_len = device_len - cached_len, table_idx, page_table (raw physical
+rows, width a multiple of 32), out_loc, positions.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import (PKV_STATUS_BAD_ALLOC, PKV_STATUS_BAD_DECODE, PKV_STATUS_BAD_LENGTHS, PKV_STATUS_BAD_OUT_LOC,
+                   PKV_STATUS_BAD_PAGE_ROW, PKV_STATUS_BAD_TABLE_IDX, PKV_STATUS_TOKEN_COUNT)
+
+__all__ = ["PagedKVError", "KVPoolTensors", "BatchTensors", "MetadataBuffers", "kv_store", "build_attn_metadata",
+           "paged_decode_attn", "paged_extend_attn", "plan_bytes", "workspace_bytes", "library_path",
+           "PKV_STATUS_BAD_ALLOC", "PKV_STATUS_BAD_DECODE", "PKV_STATUS_BAD_LENGTHS", "PKV_STATUS_BAD_OUT_LOC",
+           "PKV_STATUS_BAD_PAGE_ROW", "PKV_STATUS_BAD_TABLE_IDX", "PKV_STATUS_TOKEN_COUNT"]
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        msg = _lib.lib().pkv_error_string(code).decode()
+        if code == _lib.PKV_ERR_HIP:
+            msg += f" (hipError {_lib.lib().pkv_last_hip_error()})"
+        super().__init__(f"{fn} failed: {msg}")
+        self.code = code
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, dims=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if dims is not None and t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check(fn: str, code: int):
+    if code != _lib.PKV_OK:
+        raise PagedKVError(fn, code)
+
+
+@dataclass
+class KVPoolTensors:
+    """One layer's pool: k and v are bf16 [num_rows, Hkv, d]."""
+    k: torch.Tensor
+    v: torch.Tensor
+    page_size: int = 1
+
+    def struct(self) -> _lib.KVPool:
+        _need(self.k, "k_pool", torch.bfloat16, 3)
+        _need(self.v, "v_pool", torch.bfloat16, 3)
+        if self.k.shape != self.v.shape:
+            raise ValueError("k and v pools differ in shape")
+        n, hkv, d = self.k.shape
+        return _lib.KVPool(self.k.data_ptr(), self.v.data_ptr(), n, hkv * d, self.page_size, hkv, d, 0)
+
+
+@dataclass
+class BatchTensors:
+    """Per-request int32 device arrays and the batch's counts."""
+    table_idx: torch.Tensor
+    cached_len: torch.Tensor
+    device_len: torch.Tensor
+    num_decode: int
+    num_tokens: int
+
+    def struct(self) -> _lib.Batch:
+        for name in ("table_idx", "cached_len", "device_len"):
+            _need(getattr(self, name), name, torch.int32, 1)
+        b = self.table_idx.numel()
+        if self.cached_len.numel() != b or self.device_len.numel() != b:
+            raise ValueError("table_idx, cached_len and device_len differ in length")
+        return _lib.Batch(b, self.num_decode, self.num_tokens, self.table_idx.data_ptr(),
+                          self.cached_len.data_ptr(), self.device_len.data_ptr())
+
+
+@dataclass
+class MetadataBuffers:
+    """Caller-owned outputs of build_attn_metadata (fixed addresses)."""
+    out_loc: torch.Tensor
+    positions: torch.Tensor
+    qo_indptr: torch.Tensor
+    kv_indptr: torch.Tensor
+    last_indices: torch.Tensor
+    plan: torch.Tensor
+    status: Optional[torch.Tensor] = None
+
+    @classmethod
+    def allocate(cls, max_reqs: int, max_tokens: int, num_qo_heads: int, num_kv_heads: int,
+                 device="cuda") -> "MetadataBuffers":
+        nbytes = plan_bytes(max_reqs, max_tokens, num_qo_heads, num_kv_heads)
+        i32 = dict(dtype=torch.int32, device=device)
+        return cls(out_loc=torch.zeros(max(max_tokens, 1), **i32), positions=torch.zeros(max(max_tokens, 1), **i32),
+                   qo_indptr=torch.zeros(max_reqs + 1, **i32), kv_indptr=torch.zeros(max_reqs + 1, **i32),
+                   last_indices=torch.zeros(max(max_reqs, 1), **i32),
+                   plan=torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device),
+                   status=torch.zeros(1, **i32))
+
+    def struct(self) -> _lib.AttnMetadata:
+        for name in ("out_loc", "positions", "qo_indptr", "kv_indptr", "last_indices"):
+            _need(getattr(self, name), name, torch.int32, 1)
+        _need(self.plan, "plan", torch.uint8, 1)
+        if self.status is not None:
+            _need(self.status, "status", torch.int32, 1)
+        return _lib.AttnMetadata(self.out_loc.data_ptr(), self.positions.data_ptr(), self.qo_indptr.data_ptr(),
+                                 self.kv_indptr.data_ptr(), self.last_indices.data_ptr(), self.plan.data_ptr(),
+                                 self.plan.numel(), _ptr(self.status))
+
+
+def plan_bytes(max_reqs: int, max_tokens: int, num_qo_heads: int, num_kv_heads: int) -> int:
+    n = _lib.lib().pkv_plan_bytes(max_reqs, max_tokens, num_qo_heads, num_kv_heads)
+    if n == 0:
+        raise ValueError("invalid plan size query")
+    return n
+
+
+def workspace_bytes(max_reqs: int, num_qo_heads: int, head_dim: int = 128) -> int:
+    n = _lib.lib().paged_attn_workspace_bytes(max_reqs, num_qo_heads, head_dim)
+    if n == 0:
+        raise ValueError("invalid workspace size query")
+    return n
+
+
+def kv_store(pool: KVPoolTensors, k_new: torch.Tensor, v_new: torch.Tensor, out_loc: torch.Tensor,
+             status: Optional[torch.Tensor] = None, stream=None) -> None:
+    p = pool.struct()
+    _need(k_new, "k_new", torch.bfloat16, 3)
+    _need(v_new, "v_new", torch.bfloat16, 3)
+    _need(out_loc, "out_loc", torch.int32, 1)
+    t = k_new.shape[0]
+    if v_new.shape != k_new.shape or k_new.shape[1:] != pool.k.shape[1:] or out_loc.numel() < t:
+        raise ValueError("k_new / v_new / out_loc shapes do not match the pool")
+    if status is not None:
+        _need(status, "status", torch.int32, 1)
+    _check("kv_store", _lib.lib().kv_store(ctypes.byref(p), k_new.data_ptr(), v_new.data_ptr(), out_loc.data_ptr(),
+                                           t, _ptr(status), _stream(stream)))
+
+
+def build_attn_metadata(batch: BatchTensors, page_table: torch.Tensor, page_size: int, num_pool_rows: int,
+                        alloc_rows: torch.Tensor, num_qo_heads: int, num_kv_heads: int, meta: MetadataBuffers,
+                        stream=None) -> None:
+    b = batch.struct()
+    _need(page_table, "page_table", torch.int32, 2)
+    _need(alloc_rows, "alloc_rows", torch.int32, 1)
+    pt = _lib.PageTable(page_table.data_ptr(), page_table.shape[0], page_table.shape[1])
+    m = meta.struct()
+    _check("build_attn_metadata",
+           _lib.lib().build_attn_metadata(ctypes.byref(b), ctypes.byref(pt), page_size, num_pool_rows,
+                                          alloc_rows.data_ptr() if alloc_rows.numel() else None, alloc_rows.numel(),
+                                          num_qo_heads, num_kv_heads, ctypes.byref(m), _stream(stream)))
+
+
+def _attn(fn_name, pool, page_table, batch, meta, q, o, sm_scale, workspace, stream):
+    p = pool.struct()
+    b = batch.struct()
+    _need(page_table, "page_table", torch.int32, 2)
+    _need(q, "q", torch.bfloat16, 3)
+    _need(o, "o", torch.bfloat16, 3)
+    if q.shape != o.shape or q.shape[0] < batch.num_tokens or q.shape[2] != pool.k.shape[2]:
+        raise ValueError("q / o shapes do not match the batch and pool")
+    pt = _lib.PageTable(page_table.data_ptr(), page_table.shape[0], page_table.shape[1])
+    m = meta.struct()
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _need(workspace, "workspace", workspace.dtype, 1)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    fn = getattr(_lib.lib(), fn_name)
+    _check(fn_name, fn(ctypes.byref(p), ctypes.byref(pt), ctypes.byref(b), ctypes.byref(m), q.data_ptr(),
+                       o.data_ptr(), q.shape[1], float(sm_scale), ws_ptr, ws_bytes, _stream(stream)))
+
+
+def paged_decode_attn(pool: KVPoolTensors, page_table: torch.Tensor, batch: BatchTensors, meta: MetadataBuffers,
+                      q: torch.Tensor, o: torch.Tensor, sm_scale: float, workspace: torch.Tensor,
+                      stream=None) -> None:
+    _attn("paged_decode_attn", pool, page_table, batch, meta, q, o, sm_scale, workspace, stream)
+
+
+def paged_extend_attn(pool: KVPoolTensors, page_table: torch.Tensor, batch: BatchTensors, meta: MetadataBuffers,
+                      q: torch.Tensor, o: torch.Tensor, sm_scale: float, workspace: Optional[torch.Tensor] = None,
+                      stream=None) -> None:
+    _attn("paged_extend_attn", pool, page_table, batch, meta, q, o, sm_scale, workspace, stream)

@@ -1,0 +1,77 @@
+"""ctypes view of libpagedkv.so: the structs and prototypes of include/pagedkv.h."""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+
+PKV_OK = 0
+PKV_ERR_INVALID_ARGUMENT = 1
+PKV_ERR_UNSUPPORTED = 2
+PKV_ERR_WORKSPACE = 3
+PKV_ERR_HIP = 4
+
+PKV_STATUS_BAD_OUT_LOC = 0x01
+PKV_STATUS_BAD_LENGTHS = 0x02
+PKV_STATUS_BAD_TABLE_IDX = 0x04
+PKV_STATUS_BAD_PAGE_ROW = 0x08
+PKV_STATUS_BAD_DECODE = 0x10
+PKV_STATUS_TOKEN_COUNT = 0x20
+PKV_STATUS_BAD_ALLOC = 0x40
+
+
+class KVPool(ctypes.Structure):
+    _fields_ = [("k", c_void_p), ("v", c_void_p), ("num_rows", c_int64), ("row_stride", c_int64),
+                ("page_size", c_int32), ("num_kv_heads", c_int32), ("head_dim", c_int32), ("reserved", c_int32)]
+
+
+class PageTable(ctypes.Structure):
+    _fields_ = [("data", c_void_p), ("num_rows", c_int32), ("width", c_int32)]
+
+
+class Batch(ctypes.Structure):
+    _fields_ = [("num_reqs", c_int32), ("num_decode", c_int32), ("num_tokens", c_int64),
+                ("table_idx", c_void_p), ("cached_len", c_void_p), ("device_len", c_void_p)]
+
+
+class AttnMetadata(ctypes.Structure):
+    _fields_ = [("out_loc", c_void_p), ("positions", c_void_p), ("qo_indptr", c_void_p),
+                ("kv_indptr", c_void_p), ("last_indices", c_void_p), ("plan", c_void_p),
+                ("plan_bytes", c_size_t), ("status", c_void_p)]
+
+
+# name -> (restype, argtypes); the exports of include/pagedkv.h
+PROTOTYPES = {
+    "pkv_plan_bytes": (c_size_t, [c_int32, c_int64, c_int32, c_int32]),
+    "paged_attn_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
+    "kv_store": (c_int, [POINTER(KVPool), c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p]),
+    "build_attn_metadata": (c_int, [POINTER(Batch), POINTER(PageTable), c_int32, c_int64, c_void_p, c_int64,
+                                    c_int32, c_int32, POINTER(AttnMetadata), c_void_p]),
+    "paged_decode_attn": (c_int, [POINTER(KVPool), POINTER(PageTable), POINTER(Batch), POINTER(AttnMetadata),
+                                  c_void_p, c_void_p, c_int32, c_float, c_void_p, c_size_t, c_void_p]),
+    "paged_extend_attn": (c_int, [POINTER(KVPool), POINTER(PageTable), POINTER(Batch), POINTER(AttnMetadata),
+                                  c_void_p, c_void_p, c_int32, c_float, c_void_p, c_size_t, c_void_p]),
+    "pkv_error_string": (ctypes.c_char_p, [c_int]),
+    "pkv_last_hip_error": (c_int, []),
+    "pkv_version": (c_int, []),
+}
+
+_LIB = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built (no fallback exists)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_attention_08_amd.build` "
+                               "(the paged-KV path has no CPU fallback)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in PROTOTYPES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = handle
+    return _LIB

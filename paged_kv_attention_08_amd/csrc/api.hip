@@ -1,0 +1,235 @@
+// extern "C" entry points: host-side argument checks, then launches on the
+// caller's stream.  Nothing here allocates, frees or synchronises.
+#include <math.h>
+
+#include "kernels.hpp"
+
+using namespace pkv;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_failed(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return PKV_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool pow2_le64(int32_t s) { return s >= 1 && s <= 64 && (s & (s - 1)) == 0; }
+
+int log2i(int32_t s) {
+  int k = 0;
+  while ((1 << k) < s) ++k;
+  return k;
+}
+
+int check_heads(int32_t hq, int32_t hkv) {
+  if (hq <= 0 || hkv <= 0 || hq % hkv != 0) return PKV_ERR_INVALID_ARGUMENT;
+  if (hq / hkv > kMaxGroup) return PKV_ERR_UNSUPPORTED;
+  return PKV_OK;
+}
+
+int check_pool(const pkv_kv_pool* p) {
+  if (!p || !p->k || !p->v) return PKV_ERR_INVALID_ARGUMENT;
+  if (p->head_dim != kHeadDim) return PKV_ERR_UNSUPPORTED;
+  if (!pow2_le64(p->page_size)) return PKV_ERR_UNSUPPORTED;
+  if (p->num_kv_heads <= 0 || p->reserved != 0) return PKV_ERR_INVALID_ARGUMENT;
+  if (p->num_rows <= 0 || p->num_rows >= (int64_t(1) << 31) || p->num_rows % p->page_size != 0)
+    return PKV_ERR_INVALID_ARGUMENT;
+  if (p->row_stride < (int64_t)p->num_kv_heads * p->head_dim || p->row_stride % 8 != 0) return PKV_ERR_INVALID_ARGUMENT;
+  if (!aligned16(p->k) || !aligned16(p->v)) return PKV_ERR_INVALID_ARGUMENT;
+  return PKV_OK;
+}
+
+int check_batch(const pkv_batch* b) {
+  if (!b) return PKV_ERR_INVALID_ARGUMENT;
+  if (b->num_reqs < 0 || b->num_decode < 0 || b->num_decode > b->num_reqs) return PKV_ERR_INVALID_ARGUMENT;
+  if (b->num_tokens < 0 || b->num_tokens >= (int64_t(1) << 31)) return PKV_ERR_INVALID_ARGUMENT;
+  if (b->num_reqs > 0 && (!b->table_idx || !b->cached_len || !b->device_len)) return PKV_ERR_INVALID_ARGUMENT;
+  return PKV_OK;
+}
+
+int check_page_table(const pkv_page_table* t) {
+  if (!t || !t->data || t->num_rows <= 0 || t->width <= 0 || t->width % 32 != 0) return PKV_ERR_INVALID_ARGUMENT;
+  return PKV_OK;
+}
+
+int check_meta_common(const pkv_attn_metadata* m, const pkv_batch* b, int32_t group, PlanLayout* L) {
+  if (!m || !m->qo_indptr || !m->kv_indptr || !m->plan) return PKV_ERR_INVALID_ARGUMENT;
+  if (b->num_reqs > 0 && !m->last_indices) return PKV_ERR_INVALID_ARGUMENT;
+  if (!aligned16(m->plan)) return PKV_ERR_INVALID_ARGUMENT;
+  *L = plan_layout(b->num_reqs, b->num_tokens, group);
+  if (m->plan_bytes < (size_t)L->total) return PKV_ERR_WORKSPACE;
+  return PKV_OK;
+}
+
+int fill_attn_args(const pkv_kv_pool* pool, const pkv_page_table* pt, const pkv_batch* batch,
+                   const pkv_attn_metadata* meta, const void* q, void* o, int32_t hq, float sm_scale,
+                   AttnArgs* a) {
+  int rc;
+  if ((rc = check_pool(pool)) != PKV_OK) return rc;
+  if ((rc = check_page_table(pt)) != PKV_OK) return rc;
+  if ((rc = check_batch(batch)) != PKV_OK) return rc;
+  if ((rc = check_heads(hq, pool->num_kv_heads)) != PKV_OK) return rc;
+  if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return PKV_ERR_INVALID_ARGUMENT;
+  if (batch->num_tokens > 0 && (!q || !o || !aligned16(q) || !aligned16(o))) return PKV_ERR_INVALID_ARGUMENT;
+  PlanLayout L;
+  if ((rc = check_meta_common(meta, batch, hq / pool->num_kv_heads, &L)) != PKV_OK) return rc;
+  a->k_pool = static_cast<const uint16_t*>(pool->k);
+  a->v_pool = static_cast<const uint16_t*>(pool->v);
+  a->row_stride = pool->row_stride;
+  a->num_pool_rows = pool->num_rows;
+  a->page_table = pt->data;
+  a->R = pt->num_rows;
+  a->W = pt->width;
+  a->B = batch->num_reqs;
+  a->num_decode = batch->num_decode;
+  a->T = batch->num_tokens;
+  a->Hq = hq;
+  a->Hkv = pool->num_kv_heads;
+  a->group = hq / pool->num_kv_heads;
+  a->scale_log2 = sm_scale * 1.4426950408889634f;
+  a->table_idx = batch->table_idx;
+  a->cached_len = batch->cached_len;
+  a->device_len = batch->device_len;
+  a->qo_indptr = meta->qo_indptr;
+  a->q = static_cast<const uint16_t*>(q);
+  a->o = static_cast<uint16_t*>(o);
+  a->plan = static_cast<const char*>(meta->plan);
+  a->layout = L;
+  a->ws_acc = nullptr;
+  a->ws_ml = nullptr;
+  a->status = meta->status;
+  return PKV_OK;
+}
+
+size_t decode_ws_bytes(int32_t max_reqs, int32_t hq) {
+  const int64_t items = (int64_t)max_reqs + kDecodeTargetItems;
+  return (size_t)(items * hq * (kHeadDim + 2) * 4);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pkv_plan_bytes(int32_t max_reqs, int64_t max_tokens, int32_t num_qo_heads, int32_t num_kv_heads) {
+  if (max_reqs < 0 || max_tokens < 0 || check_heads(num_qo_heads, num_kv_heads) != PKV_OK) return 0;
+  return (size_t)plan_layout(max_reqs, max_tokens, num_qo_heads / num_kv_heads).total;
+}
+
+size_t paged_attn_workspace_bytes(int32_t max_reqs, int32_t num_qo_heads, int32_t head_dim) {
+  if (max_reqs < 0 || num_qo_heads <= 0 || head_dim != kHeadDim) return 0;
+  return decode_ws_bytes(max_reqs, num_qo_heads);
+}
+
+int kv_store(const pkv_kv_pool* pool, const void* k_new, const void* v_new, const int32_t* out_loc,
+             int64_t num_tokens, int32_t* status, void* stream) {
+  int rc = check_pool(pool);
+  if (rc != PKV_OK) return rc;
+  if (num_tokens < 0) return PKV_ERR_INVALID_ARGUMENT;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_new || !v_new || !out_loc || !aligned16(k_new) || !aligned16(v_new)) return PKV_ERR_INVALID_ARGUMENT;
+  StoreArgs a;
+  a.k_new = static_cast<const uint4*>(k_new);
+  a.v_new = static_cast<const uint4*>(v_new);
+  a.out_loc = out_loc;
+  a.k_pool = static_cast<uint4*>(pool->k);
+  a.v_pool = static_cast<uint4*>(pool->v);
+  a.num_tokens = num_tokens;
+  a.row_stride_vec = pool->row_stride / 8;
+  a.num_rows = pool->num_rows;
+  a.row_vec = pool->num_kv_heads * pool->head_dim / 8;
+  a.status = status;
+  hipError_t e = launch_kv_store(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : hip_failed(e);
+}
+
+int build_attn_metadata(const pkv_batch* batch, const pkv_page_table* page_table, int32_t page_size,
+                        int64_t num_pool_rows, const int32_t* alloc_rows, int64_t num_alloc,
+                        int32_t num_qo_heads, int32_t num_kv_heads, const pkv_attn_metadata* meta,
+                        void* stream) {
+  int rc;
+  if ((rc = check_batch(batch)) != PKV_OK) return rc;
+  if ((rc = check_page_table(page_table)) != PKV_OK) return rc;
+  if (!pow2_le64(page_size)) return PKV_ERR_UNSUPPORTED;
+  if (num_pool_rows <= 0 || num_pool_rows >= (int64_t(1) << 31) || num_pool_rows % page_size != 0)
+    return PKV_ERR_INVALID_ARGUMENT;
+  if (num_alloc < 0 || (num_alloc > 0 && !alloc_rows)) return PKV_ERR_INVALID_ARGUMENT;
+  if ((rc = check_heads(num_qo_heads, num_kv_heads)) != PKV_OK) return rc;
+  PlanLayout L;
+  if ((rc = check_meta_common(meta, batch, num_qo_heads / num_kv_heads, &L)) != PKV_OK) return rc;
+  if (batch->num_tokens > 0 && (!meta->out_loc || !meta->positions)) return PKV_ERR_INVALID_ARGUMENT;
+  MetaArgs a;
+  a.B = batch->num_reqs;
+  a.num_decode = batch->num_decode;
+  a.R = page_table->num_rows;
+  a.W = page_table->width;
+  a.page_shift = log2i(page_size);
+  a.group = num_qo_heads / num_kv_heads;
+  a.T = batch->num_tokens;
+  a.num_pool_rows = num_pool_rows;
+  a.num_alloc = num_alloc;
+  a.table_idx = batch->table_idx;
+  a.cached_len = batch->cached_len;
+  a.device_len = batch->device_len;
+  a.page_table = page_table->data;
+  a.alloc_rows = alloc_rows;
+  a.out_loc = meta->out_loc;
+  a.positions = meta->positions;
+  a.qo_indptr = meta->qo_indptr;
+  a.kv_indptr = meta->kv_indptr;
+  a.last_indices = meta->last_indices;
+  a.status = meta->status;
+  a.plan = static_cast<char*>(meta->plan);
+  a.layout = L;
+  hipError_t e = launch_metadata(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : hip_failed(e);
+}
+
+int paged_decode_attn(const pkv_kv_pool* pool, const pkv_page_table* page_table, const pkv_batch* batch,
+                      const pkv_attn_metadata* meta, const void* q, void* o, int32_t num_qo_heads,
+                      float sm_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  AttnArgs a;
+  int rc = fill_attn_args(pool, page_table, batch, meta, q, o, num_qo_heads, sm_scale, &a);
+  if (rc != PKV_OK) return rc;
+  if (batch->num_decode == 0) return PKV_OK;
+  const size_t need = decode_ws_bytes(batch->num_reqs, num_qo_heads);
+  if (!workspace || !aligned16(workspace)) return PKV_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < need) return PKV_ERR_WORKSPACE;
+  a.ws_acc = static_cast<float*>(workspace);
+  a.ws_ml = a.ws_acc + (int64_t)a.layout.cap_items * num_qo_heads * kHeadDim;
+  hipError_t e = launch_decode(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : hip_failed(e);
+}
+
+int paged_extend_attn(const pkv_kv_pool* pool, const pkv_page_table* page_table, const pkv_batch* batch,
+                      const pkv_attn_metadata* meta, const void* q, void* o, int32_t num_qo_heads,
+                      float sm_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  AttnArgs a;
+  int rc = fill_attn_args(pool, page_table, batch, meta, q, o, num_qo_heads, sm_scale, &a);
+  if (rc != PKV_OK) return rc;
+  if (batch->num_decode >= batch->num_reqs) return PKV_OK;
+  hipError_t e = launch_extend(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : hip_failed(e);
+}
+
+const char* pkv_error_string(int code) {
+  switch (code) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PKV_ERR_WORKSPACE: return "plan or workspace too small";
+    case PKV_ERR_HIP: return "HIP launch failure";
+    default: return "unknown error code";
+  }
+}
+
+int pkv_last_hip_error(void) { return g_last_hip_error; }
+
+int pkv_version(void) { return 1; }
+
+}  // extern "C"

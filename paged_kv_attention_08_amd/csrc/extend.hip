@@ -1,0 +1,232 @@
+// paged_extend_attn: chunked prefill on a cached (possibly radix-shared)
+// prefix, K/V gathered through the page table, bf16 MFMA for QK^T and PV.
+//
+// mini-sglang learning notes, Req and chunked-prefill passages: a chunk adds
+// extend_len = device_len - cached_len new tokens on top of cached_len tokens
+// already in the pool; prefill is compute bound and needs large tiles to keep
+// the matrix units busy.  Deep dive 5.2: FlashAttention tiling with an online
+// softmax keeps the n x n score matrix out of HBM.
+//
+// Work decomposition: one workgroup (4 wavefronts) per plan tile = (request,
+// TQ consecutive new tokens) and KV head g.  Its 128 rows are the
+// (token, query head) pairs of the tile that share KV head g, token-major
+// (row = tq * G + query head within the group), so each gathered K/V tile is
+// loaded once for all G query heads.  Wavefront w owns rows 32w..32w+31.
+//
+// Per 64-key tile:
+//   * the workgroup gathers 64 K rows and 64 V rows of head g (lane = key,
+//     wavefront = 32-wide d range, 4 x 16-byte loads each) into registers one
+//     tile ahead, then writes K row-major to LDS and V transposed (d-major);
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys x rows): the K operand
+//     is read from LDS, Q stays in registers for the whole loop.  In the
+//     32x32 accumulator layout each lane owns one row (query) and 16 of its 32
+//     keys, so the row max needs one cross-half shuffle;
+//   * causal masking is applied only on tiles that reach past the first
+//     row's position; prefix tiles are unmasked;
+//   * online softmax in fp32 (the max moves only when it grows by more than
+//     2^8, so the output accumulator is rarely rescaled);
+//   * O^T += V^T P^T: the probabilities, rounded to bf16, are used as the B
+//     operand straight from the score accumulator registers (the key order of
+//     the contraction is permuted to match them); the V^T operand is read from
+//     the transposed LDS tile.
+#include "kernels.hpp"
+
+namespace pkv {
+
+namespace {
+
+constexpr int kKeyTile = 64;
+constexpr int kKsStride = 136;  // bf16 elements per K row in LDS (128 + 8 pad)
+constexpr int kVtStride = 68;   // bf16 elements per V^T row in LDS (64 keys + 4 pad)
+
+__device__ inline bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ inline uint4 load16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__global__ void __launch_bounds__(256, 2) extend_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t ks[kKeyTile * kKsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[kHeadDim * kVtStride];
+
+  const int32_t* header = reinterpret_cast<const int32_t*>(a.plan);
+  const int tile = blockIdx.x;
+  const int g = blockIdx.y;
+  if (tile >= header[2]) return;  // uniform for the workgroup
+
+  const int2 tl = reinterpret_cast<const int2*>(a.plan + a.layout.tiles_off)[tile];
+  const int i = tl.x;
+  const int t0 = tl.y;
+  const int32_t c = a.cached_len[i];
+  const int32_t dl = a.device_len[i];
+  const int64_t tokbase = a.qo_indptr[i];
+  const int G = a.group;
+  const int TQ = a.layout.tile_q;
+  const int n_tok = min(TQ, dl - c - t0);
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int row = wave * 32 + l32;
+  const int tq = row / G;
+  const int gh = row - tq * G;
+  const int64_t token = tokbase + t0 + tq;
+  const bool row_valid = (tq < n_tok) && token >= 0 && token < a.T;
+  const int pos = row_valid ? c + t0 + tq : -1;
+  const int h = g * G + gh;
+
+  bf16x8 qop[8];
+  {
+    const uint16_t* qrow = a.q + (token * a.Hq + h) * kHeadDim + half * 8;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) qop[kk] = as_bf16x8(row_valid ? load16(qrow + 16 * kk) : make_uint4(0, 0, 0, 0));
+  }
+
+  const int kv_end = min(dl, c + t0 + n_tok);
+  const int32_t* pt_row = a.page_table + (int64_t)a.table_idx[i] * a.W;
+  const uint16_t* kbase = a.k_pool + (int64_t)g * kHeadDim + wave * 32;
+  const uint16_t* vbase = a.v_pool + (int64_t)g * kHeadDim + wave * 32;
+
+  uint4 kpre[4], vpre[4];
+  auto gather = [&](int kt) {
+    const int key = kt + lane;
+    int64_t prow = -1;
+    if (key < kv_end) {
+      const int32_t e = pt_row[key];
+      if (e >= 0 && (int64_t)e < a.num_pool_rows) prow = e;
+      else raise_status(a.status, PKV_STATUS_BAD_PAGE_ROW);
+    }
+    const uint16_t* kp = kbase + (prow < 0 ? 0 : prow) * a.row_stride;
+    const uint16_t* vp = vbase + (prow < 0 ? 0 : prow) * a.row_stride;
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      kpre[cc] = prow >= 0 ? load16(kp + cc * 8) : make_uint4(0, 0, 0, 0);
+      vpre[cc] = prow >= 0 ? load16(vp + cc * 8) : make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  f32x16 oacc[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) oacc[nb][v] = 0.f;
+  float m = -INFINITY;
+  float lsum = 0.f;
+  const float csc = a.scale_log2;
+  const int min_pos = c + t0;
+
+  gather(0);
+  for (int kt = 0; kt < kv_end; kt += kKeyTile) {
+    __syncthreads();
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      *reinterpret_cast<uint4*>(&ks[lane * kKsStride + wave * 32 + cc * 8]) = kpre[cc];
+      const uint32_t w4[4] = {vpre[cc].x, vpre[cc].y, vpre[cc].z, vpre[cc].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vt[(wave * 32 + cc * 8 + 2 * e) * kVtStride + lane] = (uint16_t)(w4[e] & 0xffffu);
+        vt[(wave * 32 + cc * 8 + 2 * e + 1) * kVtStride + lane] = (uint16_t)(w4[e] >> 16);
+      }
+    }
+    __syncthreads();
+    if (kt + kKeyTile < kv_end) gather(kt + kKeyTile);
+
+    // S^T = K Q^T : two 32-key blocks
+    f32x16 sacc[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sacc[mb][v] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const bf16x8 kop = as_bf16x8(*reinterpret_cast<const uint4*>(&ks[(mb * 32 + l32) * kKsStride + half * 8 + 16 * kk]));
+        sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[kk], sacc[mb], 0, 0, 0);
+      }
+    }
+    // element v of block mb is key kt + 32 mb + 8 (v / 4) + 4 half + v % 4 of row l32
+    const bool need_mask = kt + kKeyTile - 1 > min_pos;
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float s = sacc[mb][v] * csc;
+        if (need_mask) {
+          const int key = kt + 32 * mb + 8 * (v >> 2) + 4 * half + (v & 3);
+          if (key > pos) s = -INFINITY;
+        }
+        sacc[mb][v] = s;
+        tmax = fmaxf(tmax, s);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const bool upd = tmax > m + 8.f;
+    float alpha = 1.f;
+    if (upd) {
+      alpha = fast_exp2(m - tmax);
+      m = tmax;
+    }
+    if (__ballot(upd) != 0) {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[nb][v] *= alpha;
+    }
+    const float ms = (m == -INFINITY) ? 0.f : m;
+    float psum = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float p = fast_exp2(sacc[mb][v] - ms);
+        sacc[mb][v] = p;
+        psum += p;
+      }
+    lsum = lsum * alpha + psum;
+
+    // O^T += V^T P^T, 16 keys per MFMA
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq) {
+        uint4 pw;
+        pw.x = pack_bf16x2(sacc[mb][8 * kq + 0], sacc[mb][8 * kq + 1]);
+        pw.y = pack_bf16x2(sacc[mb][8 * kq + 2], sacc[mb][8 * kq + 3]);
+        pw.z = pack_bf16x2(sacc[mb][8 * kq + 4], sacc[mb][8 * kq + 5]);
+        pw.w = pack_bf16x2(sacc[mb][8 * kq + 6], sacc[mb][8 * kq + 7]);
+        const bf16x8 pop = as_bf16x8(pw);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const uint16_t* vrow = &vt[(nb * 32 + l32) * kVtStride + mb * 32 + 16 * kq + 4 * half];
+          const uint2 lo4 = *reinterpret_cast<const uint2*>(vrow);
+          const uint2 hi4 = *reinterpret_cast<const uint2*>(vrow + 8);
+          const bf16x8 vop = as_bf16x8(make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
+          oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, oacc[nb], 0, 0, 0);
+        }
+      }
+  }
+
+  const float L = lsum + __shfl_xor(lsum, 32, 64);
+  if (row_valid) {
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    uint16_t* orow = a.o + (token * a.Hq + h) * kHeadDim;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = nb * 32 + 8 * q4 + 4 * half;
+        uint2 out;
+        out.x = pack_bf16x2(oacc[nb][4 * q4 + 0] * inv, oacc[nb][4 * q4 + 1] * inv);
+        out.y = pack_bf16x2(oacc[nb][4 * q4 + 2] * inv, oacc[nb][4 * q4 + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + d0) = out;
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_extend(const AttnArgs& a, hipStream_t s) {
+  if (a.num_decode >= a.B) return hipSuccess;
+  const dim3 grid((unsigned)a.layout.cap_tiles, (unsigned)a.Hkv);
+  hipLaunchKernelGGL(extend_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,68 @@
+// Kernel argument blocks and launchers (internal to the library).
+#pragma once
+
+#include "common.hpp"
+
+namespace pkv {
+
+struct StoreArgs {
+  const uint4* k_new;
+  const uint4* v_new;
+  const int32_t* out_loc;
+  uint4* k_pool;
+  uint4* v_pool;
+  int64_t num_tokens;
+  int64_t row_stride_vec;  // 16-byte vectors between pool rows
+  int64_t num_rows;
+  int32_t row_vec;         // 16-byte vectors per new row (Hkv * d * 2 / 16)
+  int32_t* status;
+};
+
+struct MetaArgs {
+  int32_t B, num_decode, R, W, page_shift, group;
+  int64_t T, num_pool_rows, num_alloc;
+  const int32_t* table_idx;
+  const int32_t* cached_len;
+  const int32_t* device_len;
+  int32_t* page_table;
+  const int32_t* alloc_rows;
+  int32_t* out_loc;
+  int32_t* positions;
+  int32_t* qo_indptr;
+  int32_t* kv_indptr;
+  int32_t* last_indices;
+  int32_t* status;
+  char* plan;
+  PlanLayout layout;
+};
+
+struct AttnArgs {
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  int64_t row_stride;      // bf16 elements
+  int64_t num_pool_rows;
+  const int32_t* page_table;
+  int32_t R, W;
+  int32_t B, num_decode;
+  int64_t T;
+  int32_t Hq, Hkv, group;
+  float scale_log2;        // sm_scale * log2(e)
+  const int32_t* table_idx;
+  const int32_t* cached_len;
+  const int32_t* device_len;
+  const int32_t* qo_indptr;
+  const uint16_t* q;
+  uint16_t* o;
+  const char* plan;
+  PlanLayout layout;
+  float* ws_acc;           // [cap_items, Hq, d]
+  float* ws_ml;            // [cap_items, Hq, 2] (running max in log2 units, running sum)
+  int32_t* status;
+};
+
+hipError_t launch_kv_store(const StoreArgs& a, hipStream_t s);
+hipError_t launch_metadata(const MetaArgs& a, hipStream_t s);
+hipError_t launch_decode(const AttnArgs& a, hipStream_t s);
+hipError_t launch_extend(const AttnArgs& a, hipStream_t s);
+
+}  // namespace pkv

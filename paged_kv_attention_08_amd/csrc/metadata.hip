@@ -1,0 +1,233 @@
+// build_attn_metadata: page-table write for the batch's new tokens, out_loc,
+// positions, running totals and the attention plan.
+//
+// mini-sglang learning notes, page-table passage: the scheduler counts, page
+// aligned, the new pages each request needs for [cached_len, device_len),
+// takes them from free_slots and writes the page table with raw physical
+// positions; the Batch then carries positions and out_loc.  "SGLang source
+// guide", main line 3: the same quantities are seq_lens, extend_prefix_lens,
+// extend_seq_lens, req_pool_indices and out_cache_loc.
+//
+// Two launches on the caller's stream:
+//   plan_kernel  (one workgroup): per-request validation, running totals
+//                (qo_indptr, kv_indptr, last_indices, alloc offsets), the
+//                decode split-K item list and the extend tile list;
+//   token_kernel (one thread per new token): finds its request by binary
+//                search over qo_indptr and writes page_table, out_loc and
+//                positions.
+// Integer work only; results are bit-exact by construction.
+#include "kernels.hpp"
+
+namespace pkv {
+
+namespace {
+
+constexpr int kPlanThreads = 256;
+constexpr int kPlanWaves = kPlanThreads / 64;
+constexpr int kScanVals = 5;
+
+struct ReqInfo {
+  bool valid;
+  int32_t ext, dl, new_pages, items, tiles;
+};
+
+__device__ inline int32_t ceil_div_pow2(int32_t x, int32_t shift) {
+  return (x + (1 << shift) - 1) >> shift;
+}
+
+__device__ inline bool request_ok(const MetaArgs& a, int i, int32_t* bits) {
+  const int32_t r = a.table_idx[i];
+  const int32_t c = a.cached_len[i];
+  const int32_t dl = a.device_len[i];
+  bool ok = true;
+  if (r < 0 || r >= a.R) { *bits |= PKV_STATUS_BAD_TABLE_IDX; ok = false; }
+  if (c < 0 || c > dl || dl > a.W) { *bits |= PKV_STATUS_BAD_LENGTHS; ok = false; }
+  if (i < a.num_decode && dl - c != 1) { *bits |= PKV_STATUS_BAD_DECODE; ok = false; }
+  return ok;
+}
+
+// Exclusive scan of kScanVals ints over the whole workgroup; returns totals.
+__device__ inline void block_scan(int32_t (&v)[kScanVals], int32_t (&excl)[kScanVals],
+                                  int32_t (&tot)[kScanVals], int32_t (*smem)[kPlanWaves]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int32_t inc[kScanVals];
+#pragma unroll
+  for (int q = 0; q < kScanVals; ++q) {
+    int32_t x = v[q];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int32_t y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    inc[q] = x;
+    if (lane == 63) smem[q][wave] = x;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kScanVals; ++q) {
+    int32_t before = 0, all = 0;
+    for (int w = 0; w < kPlanWaves; ++w) {
+      const int32_t s = smem[q][w];
+      if (w < wave) before += s;
+      all += s;
+    }
+    excl[q] = before + inc[q] - v[q];
+    tot[q] = all;
+  }
+  __syncthreads();
+}
+
+__global__ void __launch_bounds__(kPlanThreads) plan_kernel(MetaArgs a) {
+  __shared__ int32_t smem[kScanVals][kPlanWaves];
+  __shared__ long long red[kPlanWaves];
+  const int tid = threadIdx.x;
+  int32_t bits = 0;
+  int32_t* header = (int32_t*)a.plan;
+  int4* items = (int4*)(a.plan + a.layout.items_off);
+  int32_t* req_items = (int32_t*)(a.plan + a.layout.req_items_off);
+  int2* tiles = (int2*)(a.plan + a.layout.tiles_off);
+  int32_t* alloc_ptr = (int32_t*)(a.plan + a.layout.alloc_ptr_off);
+  const int32_t s = a.page_shift;
+  const int32_t tq = a.layout.tile_q;
+
+  // Pass 1: total keys of valid decode requests -> split size.
+  long long keys = 0;
+  for (int i = tid; i < a.num_decode; i += kPlanThreads) {
+    int32_t dummy = 0;
+    if (request_ok(a, i, &dummy)) keys += a.device_len[i];
+  }
+  for (int off = 32; off > 0; off >>= 1) keys += __shfl_xor(keys, off, 64);
+  if ((tid & 63) == 0) red[tid >> 6] = keys;
+  __syncthreads();
+  long long total_keys = 0;
+  for (int w = 0; w < kPlanWaves; ++w) total_keys += red[w];
+  // Split size: a multiple of 64 keys, at least 64, chosen so that the item
+  // count stays within cap_items = B + kDecodeTargetItems:
+  //   sum ceil(dl / chunk) <= total / chunk + B <= kDecodeTargetItems + B.
+  long long per = (total_keys + kDecodeTargetItems - 1) / kDecodeTargetItems;
+  int32_t chunk = (int32_t)align_up64(per > 64 ? per : 64, 64);
+
+  // Pass 2: running totals and work lists, 1024 requests at a time.
+  int32_t carry[kScanVals] = {0, 0, 0, 0, 0};
+  if (tid == 0) {
+    a.qo_indptr[0] = 0;
+    a.kv_indptr[0] = 0;
+    req_items[0] = 0;
+    alloc_ptr[0] = 0;
+  }
+  for (int base = 0; base < a.B; base += kPlanThreads) {
+    const int i = base + tid;
+    ReqInfo ri = {false, 0, 0, 0, 0, 0};
+    if (i < a.B) {
+      const int32_t c = a.cached_len[i];
+      const int32_t dl = a.device_len[i];
+      ri.valid = request_ok(a, i, &bits);
+      ri.ext = dl > c && c >= 0 ? dl - c : 0;
+      ri.dl = dl > 0 ? dl : 0;
+      ri.new_pages = (c >= 0 && c <= dl) ? ceil_div_pow2(dl, s) - ceil_div_pow2(c, s) : 0;
+      if (ri.valid) {
+        if (i < a.num_decode) ri.items = (dl + chunk - 1) / chunk;
+        else ri.tiles = (ri.ext + tq - 1) / tq;
+      }
+    }
+    int32_t v[kScanVals] = {ri.ext, ri.dl, ri.new_pages, ri.items, ri.tiles};
+    int32_t ex[kScanVals], tot[kScanVals];
+    block_scan(v, ex, tot, smem);
+    if (i < a.B) {
+      const int32_t qo_end = carry[0] + ex[0] + ri.ext;
+      a.qo_indptr[i + 1] = qo_end;
+      a.kv_indptr[i + 1] = carry[1] + ex[1] + ri.dl;
+      a.last_indices[i] = qo_end - 1;
+      alloc_ptr[i + 1] = carry[2] + ex[2] + ri.new_pages;
+      const int32_t ib = carry[3] + ex[3];
+      const int32_t cap_i = a.layout.cap_items;
+      req_items[i + 1] = min(ib + ri.items, cap_i);
+      for (int k = 0; k < ri.items && ib + k < cap_i; ++k) {
+        const int32_t k0 = k * chunk;
+        const int32_t k1 = min(ri.dl, k0 + chunk);
+        items[ib + k] = make_int4(i, k0, k1, ri.items);
+      }
+      const int32_t tb = carry[4] + ex[4];
+      const int32_t cap_t = a.layout.cap_tiles;
+      for (int k = 0; k < ri.tiles && tb + k < cap_t; ++k) {
+        // longest tiles (largest token offset, most keys) first
+        tiles[tb + k] = make_int2(i, (ri.tiles - 1 - k) * tq);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kScanVals; ++q) carry[q] += tot[q];
+  }
+  if (tid == 0) {
+    header[0] = min(carry[3], a.layout.cap_items);
+    header[1] = chunk;
+    header[2] = min(carry[4], a.layout.cap_tiles);
+    header[3] = tq;
+    header[4] = a.layout.cap_items;
+    header[5] = a.layout.cap_tiles;
+    if ((int64_t)carry[0] != a.T) bits |= PKV_STATUS_TOKEN_COUNT;
+    if ((int64_t)carry[2] > a.num_alloc) bits |= PKV_STATUS_BAD_ALLOC;
+  }
+  if (bits) raise_status(a.status, bits);
+}
+
+__global__ void __launch_bounds__(256) token_kernel(MetaArgs a) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= a.T) return;
+  const int32_t* alloc_ptr = (const int32_t*)(a.plan + a.layout.alloc_ptr_off);
+  if (t >= a.qo_indptr[a.B]) return;  // fewer new tokens than num_tokens (flagged by plan_kernel)
+  // request i: qo_indptr[i] <= t < qo_indptr[i + 1]
+  int lo = 0, hi = a.B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.qo_indptr[mid] <= t) lo = mid;
+    else hi = mid;
+  }
+  const int i = lo;
+  int32_t bits = 0;
+  if (!request_ok(a, i, &bits)) return;  // already reported by plan_kernel
+  const int32_t r = a.table_idx[i];
+  const int32_t c = a.cached_len[i];
+  const int32_t j = c + (int32_t)(t - a.qo_indptr[i]);
+  const int32_t s = a.page_shift;
+  const int32_t slot = j & ((1 << s) - 1);
+  const int32_t first_new_page = ceil_div_pow2(c, s);
+  const int32_t lp = j >> s;
+  int64_t row;
+  int32_t* pt_row = a.page_table + (int64_t)r * a.W;
+  if (lp < first_new_page) {
+    // the request's partially filled last cached page
+    row = (int64_t)pt_row[j - slot] + slot;
+    if (row < 0 || row >= a.num_pool_rows) bits |= PKV_STATUS_BAD_PAGE_ROW;
+  } else {
+    const int64_t ai = (int64_t)alloc_ptr[i] + (lp - first_new_page);
+    if (ai >= a.num_alloc) {
+      bits |= PKV_STATUS_BAD_ALLOC;
+      row = -1;
+    } else {
+      const int32_t pr = a.alloc_rows[ai];
+      row = (int64_t)pr + slot;
+      if (pr < 0 || (pr & ((1 << s) - 1)) != 0 || row >= a.num_pool_rows) bits |= PKV_STATUS_BAD_ALLOC;
+    }
+  }
+  if (bits) {
+    raise_status(a.status, bits);
+    return;
+  }
+  pt_row[j] = (int32_t)row;
+  a.out_loc[t] = (int32_t)row;
+  a.positions[t] = j;
+}
+
+}  // namespace
+
+hipError_t launch_metadata(const MetaArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.T == 0) return e;
+  const int64_t blocks = (a.T + 255) / 256;
+  hipLaunchKernelGGL(token_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace pkv
