@@ -109,6 +109,9 @@ def main(argv=None):
     ap.add_argument("--flush", action="store_true", help="flush L2/MALL before every step (outside the events)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (torch copy_) 5 times: the known-size reference "
+                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -126,6 +129,16 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        nbytes = 1 << 30
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": nbytes, "copy_calibration_bytes_written": nbytes,
+                          "launches": 5}), flush=True)
+        return 0
     log(f"generating config {args.config}")
     w = configs.FULL[args.config]()
     log(w.summary())

@@ -5,7 +5,9 @@ import ctypes
 import os
 from ctypes import POINTER, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+# PAGEDKV_LIB selects another build of the same library (for example one built
+# with different tile sizes); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("PAGEDKV_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
 
 PKV_OK = 0
 PKV_ERR_INVALID_ARGUMENT = 1

@@ -56,11 +56,11 @@ int check_page_table(const pkv_page_table* t) {
   return PKV_OK;
 }
 
-int check_meta_common(const pkv_attn_metadata* m, const pkv_batch* b, int32_t group, PlanLayout* L) {
+int check_meta_common(const pkv_attn_metadata* m, const pkv_batch* b, int32_t group, int32_t hkv, PlanLayout* L) {
   if (!m || !m->qo_indptr || !m->kv_indptr || !m->plan) return PKV_ERR_INVALID_ARGUMENT;
   if (b->num_reqs > 0 && !m->last_indices) return PKV_ERR_INVALID_ARGUMENT;
   if (!aligned16(m->plan)) return PKV_ERR_INVALID_ARGUMENT;
-  *L = plan_layout(b->num_reqs, b->num_tokens, group);
+  *L = plan_layout(b->num_reqs, b->num_tokens, group, hkv);
   if (m->plan_bytes < (size_t)L->total) return PKV_ERR_WORKSPACE;
   return PKV_OK;
 }
@@ -76,7 +76,7 @@ int fill_attn_args(const pkv_kv_pool* pool, const pkv_page_table* pt, const pkv_
   if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return PKV_ERR_INVALID_ARGUMENT;
   if (batch->num_tokens > 0 && (!q || !o || !aligned16(q) || !aligned16(o))) return PKV_ERR_INVALID_ARGUMENT;
   PlanLayout L;
-  if ((rc = check_meta_common(meta, batch, hq / pool->num_kv_heads, &L)) != PKV_OK) return rc;
+  if ((rc = check_meta_common(meta, batch, hq / pool->num_kv_heads, pool->num_kv_heads, &L)) != PKV_OK) return rc;
   a->k_pool = static_cast<const uint16_t*>(pool->k);
   a->v_pool = static_cast<const uint16_t*>(pool->v);
   a->row_stride = pool->row_stride;
@@ -116,7 +116,7 @@ extern "C" {
 
 size_t pkv_plan_bytes(int32_t max_reqs, int64_t max_tokens, int32_t num_qo_heads, int32_t num_kv_heads) {
   if (max_reqs < 0 || max_tokens < 0 || check_heads(num_qo_heads, num_kv_heads) != PKV_OK) return 0;
-  return (size_t)plan_layout(max_reqs, max_tokens, num_qo_heads / num_kv_heads).total;
+  return (size_t)plan_layout(max_reqs, max_tokens, num_qo_heads / num_kv_heads, num_kv_heads).total;
 }
 
 size_t paged_attn_workspace_bytes(int32_t max_reqs, int32_t num_qo_heads, int32_t head_dim) {
@@ -159,7 +159,7 @@ int build_attn_metadata(const pkv_batch* batch, const pkv_page_table* page_table
   if (num_alloc < 0 || (num_alloc > 0 && !alloc_rows)) return PKV_ERR_INVALID_ARGUMENT;
   if ((rc = check_heads(num_qo_heads, num_kv_heads)) != PKV_OK) return rc;
   PlanLayout L;
-  if ((rc = check_meta_common(meta, batch, num_qo_heads / num_kv_heads, &L)) != PKV_OK) return rc;
+  if ((rc = check_meta_common(meta, batch, num_qo_heads / num_kv_heads, num_kv_heads, &L)) != PKV_OK) return rc;
   if (batch->num_tokens > 0 && (!meta->out_loc || !meta->positions)) return PKV_ERR_INVALID_ARGUMENT;
   MetaArgs a;
   a.B = batch->num_reqs;

@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/pagedkv.h"
+#include "pagedkv.h"
 
 namespace pkv {
 
@@ -30,15 +30,18 @@ constexpr int kPlanHeaderInts = 16;
 // alloc_ptr      : int32 [B + 1]     first alloc_rows entry of each request
 struct PlanLayout {
   int64_t items_off, req_items_off, tiles_off, alloc_ptr_off, total;
-  int32_t cap_items, cap_tiles, tile_q;
+  int32_t cap_items, cap_tiles, tile_q, kv_groups;
 };
 
 __host__ __device__ inline int64_t align_up64(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 __host__ __device__ inline int32_t extend_tile_tokens(int32_t group) { return kExtendRows / group; }
 
-__host__ inline PlanLayout plan_layout(int32_t max_reqs, int64_t max_tokens, int32_t group) {
+constexpr int kDecodeHeadsPerGroup = 4;  // KV heads per decode workgroup
+
+__host__ inline PlanLayout plan_layout(int32_t max_reqs, int64_t max_tokens, int32_t group, int32_t num_kv_heads) {
   PlanLayout L;
+  L.kv_groups = (num_kv_heads + kDecodeHeadsPerGroup - 1) / kDecodeHeadsPerGroup;
   const int32_t tq = extend_tile_tokens(group);
   L.tile_q = tq;
   L.cap_items = max_reqs + kDecodeTargetItems;

@@ -86,20 +86,27 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(AttnArgs a) {
   const uint16_t* vbase = a.v_pool + (int64_t)g * kHeadDim + wave * 32;
 
   uint4 kpre[4], vpre[4];
+  // Unconditional gather: a key past kv_end re-reads the last valid key's
+  // row (its score is masked) and its V is zeroed before it reaches LDS.
   auto gather = [&](int kt) {
     const int key = kt + lane;
-    int64_t prow = -1;
-    if (key < kv_end) {
-      const int32_t e = pt_row[key];
-      if (e >= 0 && (int64_t)e < a.num_pool_rows) prow = e;
-      else raise_status(a.status, PKV_STATUS_BAD_PAGE_ROW);
+    int64_t prow = pt_row[min(key, kv_end - 1)];
+    if (prow < 0 || prow >= a.num_pool_rows) {
+      raise_status(a.status, PKV_STATUS_BAD_PAGE_ROW);
+      prow = 0;
     }
-    const uint16_t* kp = kbase + (prow < 0 ? 0 : prow) * a.row_stride;
-    const uint16_t* vp = vbase + (prow < 0 ? 0 : prow) * a.row_stride;
+    const uint16_t* kp = kbase + prow * a.row_stride;
+    const uint16_t* vp = vbase + prow * a.row_stride;
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
-      kpre[cc] = prow >= 0 ? load16(kp + cc * 8) : make_uint4(0, 0, 0, 0);
-      vpre[cc] = prow >= 0 ? load16(vp + cc * 8) : make_uint4(0, 0, 0, 0);
+      kpre[cc] = load16(kp + cc * 8);
+      vpre[cc] = load16(vp + cc * 8);
+    }
+  };
+  auto zero_tail = [&](int kt) {
+    if (kt + kKeyTile > kv_end && kt + lane >= kv_end) {
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) vpre[cc] = make_uint4(0, 0, 0, 0);
     }
   };
 
@@ -116,6 +123,7 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(AttnArgs a) {
   gather(0);
   for (int kt = 0; kt < kv_end; kt += kKeyTile) {
     __syncthreads();
+    zero_tail(kt);
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
       *reinterpret_cast<uint4*>(&ks[lane * kKsStride + wave * 32 + cc * 8]) = kpre[cc];
