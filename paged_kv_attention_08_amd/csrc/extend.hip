@@ -14,21 +14,29 @@
 // loaded once for all G query heads.  Wavefront w owns rows 32w..32w+31.
 //
 // Per 64-key tile:
-//   * the workgroup gathers 64 K rows and 64 V rows of head g (lane = key,
-//     wavefront = 32-wide d range, 4 x 16-byte loads each) into registers one
-//     tile ahead, then writes K row-major to LDS and V transposed (d-major);
+//   * the workgroup gathers 64 K rows and 64 V rows of head g into registers
+//     one tile ahead: wavefront w takes keys 16w..16w+15, each 16-lane group
+//     one whole 256-byte head row per load (16 bytes per lane), so a load
+//     instruction touches 4 rows.  (With one key per lane, every instruction
+//     touched 64 scattered rows and half the address translations missed the
+//     per-CU TLB.)  Both tiles are stored row-major ([key][d]) in LDS as
+//     contiguous 256-byte runs;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys x rows): the K operand
 //     is read from LDS, Q stays in registers for the whole loop.  In the
 //     32x32 accumulator layout each lane owns one row (query) and 16 of its 32
 //     keys, so the row max needs one cross-half shuffle;
 //   * causal masking is applied only on tiles that reach past the first
-//     row's position; prefix tiles are unmasked;
+//     row's position (a separately compiled loop); prefix tiles run unmasked;
 //   * online softmax in fp32 (the max moves only when it grows by more than
 //     2^8, so the output accumulator is rarely rescaled);
 //   * O^T += V^T P^T: the probabilities, rounded to bf16, are used as the B
 //     operand straight from the score accumulator registers (the key order of
-//     the contraction is permuted to match them); the V^T operand is read from
-//     the transposed LDS tile.
+//     the contraction is permuted to match them); the V^T operand (8 keys of
+//     one d per lane) comes from the row-major V tile through two gfx950 LDS
+//     transpose reads (ds_read_b64_tr_b16): in each 16-lane group, lane j
+//     addresses 4 dims of key (j / 4) and lane i receives dim i of 4 keys.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace pkv {
@@ -37,14 +45,16 @@ namespace {
 
 constexpr int kKeyTile = 64;
 constexpr int kKsStride = 136;  // bf16 elements per K row in LDS (128 + 8 pad)
-constexpr int kVtStride = 68;   // bf16 elements per V^T row in LDS (64 keys + 4 pad)
+constexpr int kVsStride = 160;  // bf16 elements per V row in LDS (80 dwords: 4 rows x 16 dwords hit 64 distinct banks)
+
+typedef short v4s __attribute__((ext_vector_type(4)));
 
 __device__ inline bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ inline uint4 load16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
 __global__ void __launch_bounds__(256, 2) extend_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t ks[kKeyTile * kKsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[kHeadDim * kVtStride];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[kKeyTile * kVsStride];
 
   const int32_t* header = reinterpret_cast<const int32_t*>(a.plan);
   const int tile = blockIdx.x;
@@ -82,31 +92,32 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(AttnArgs a) {
 
   const int kv_end = min(dl, c + t0 + n_tok);
   const int32_t* pt_row = a.page_table + (int64_t)a.table_idx[i] * a.W;
-  const uint16_t* kbase = a.k_pool + (int64_t)g * kHeadDim + wave * 32;
-  const uint16_t* vbase = a.v_pool + (int64_t)g * kHeadDim + wave * 32;
+  const uint16_t* kbase = a.k_pool + (int64_t)g * kHeadDim + (lane & 15) * 8;
+  const uint16_t* vbase = a.v_pool + (int64_t)g * kHeadDim + (lane & 15) * 8;
 
+  // loader: load u (0..3) of lane l moves 16 bytes (dims 8 (l % 16) ..) of key
+  // 16 w + 4 u + l / 16 of the tile
   uint4 kpre[4], vpre[4];
-  // Unconditional gather: a key past kv_end re-reads the last valid key's
-  // row (its score is masked) and its V is zeroed before it reaches LDS.
   auto gather = [&](int kt) {
-    const int key = kt + lane;
-    int64_t prow = pt_row[min(key, kv_end - 1)];
-    if (prow < 0 || prow >= a.num_pool_rows) {
+    // lane l fetches the entry of key kt + l; rows are then broadcast by shuffles.
+    // Keys past kv_end re-read the last valid key's row (masked, V zeroed).
+    int32_t ent = pt_row[min(kt + lane, kv_end - 1)];
+    if (ent < 0 || (int64_t)ent >= a.num_pool_rows) {
       raise_status(a.status, PKV_STATUS_BAD_PAGE_ROW);
-      prow = 0;
+      ent = 0;
     }
-    const uint16_t* kp = kbase + prow * a.row_stride;
-    const uint16_t* vp = vbase + prow * a.row_stride;
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      kpre[cc] = load16(kp + cc * 8);
-      vpre[cc] = load16(vp + cc * 8);
+    for (int u = 0; u < 4; ++u) {
+      const int64_t prow = __shfl(ent, 16 * wave + 4 * u + (lane >> 4), 64);
+      kpre[u] = load16(kbase + prow * a.row_stride);
+      vpre[u] = load16(vbase + prow * a.row_stride);
     }
   };
   auto zero_tail = [&](int kt) {
-    if (kt + kKeyTile > kv_end && kt + lane >= kv_end) {
+    if (kt + kKeyTile > kv_end) {
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) vpre[cc] = make_uint4(0, 0, 0, 0);
+      for (int u = 0; u < 4; ++u)
+        if (kt + 16 * wave + 4 * u + (lane >> 4) >= kv_end) vpre[u] = make_uint4(0, 0, 0, 0);
     }
   };
 
@@ -120,24 +131,22 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(AttnArgs a) {
   const float csc = a.scale_log2;
   const int min_pos = c + t0;
 
-  gather(0);
-  for (int kt = 0; kt < kv_end; kt += kKeyTile) {
+  // One 64-key tile.  MASK: the tile reaches past the first row's position,
+  // so keys beyond a row's own position are masked (diagonal and ragged end).
+  auto key_tile = [&](int kt, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     __syncthreads();
-    zero_tail(kt);
+    if (MASK) zero_tail(kt);
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      *reinterpret_cast<uint4*>(&ks[lane * kKsStride + wave * 32 + cc * 8]) = kpre[cc];
-      const uint32_t w4[4] = {vpre[cc].x, vpre[cc].y, vpre[cc].z, vpre[cc].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vt[(wave * 32 + cc * 8 + 2 * e) * kVtStride + lane] = (uint16_t)(w4[e] & 0xffffu);
-        vt[(wave * 32 + cc * 8 + 2 * e + 1) * kVtStride + lane] = (uint16_t)(w4[e] >> 16);
-      }
+    for (int u = 0; u < 4; ++u) {
+      const int key = 16 * wave + 4 * u + (lane >> 4);
+      *reinterpret_cast<uint4*>(&ks[key * kKsStride + (lane & 15) * 8]) = kpre[u];
+      *reinterpret_cast<uint4*>(&vs[key * kVsStride + (lane & 15) * 8]) = vpre[u];
     }
     __syncthreads();
     if (kt + kKeyTile < kv_end) gather(kt + kKeyTile);
 
-    // S^T = K Q^T : two 32-key blocks
+    // S^T = K Q^T : two 32-key blocks (raw scores, scale folded into exp below)
     f32x16 sacc[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -150,21 +159,19 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(AttnArgs a) {
       }
     }
     // element v of block mb is key kt + 32 mb + 8 (v / 4) + 4 half + v % 4 of row l32
-    const bool need_mask = kt + kKeyTile - 1 > min_pos;
+    if (MASK) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (kt + 32 * mb + 8 * (v >> 2) + 4 * half + (v & 3) > pos) sacc[mb][v] = -INFINITY;
+    }
     float tmax = -INFINITY;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float s = sacc[mb][v] * csc;
-        if (need_mask) {
-          const int key = kt + 32 * mb + 8 * (v >> 2) + 4 * half + (v & 3);
-          if (key > pos) s = -INFINITY;
-        }
-        sacc[mb][v] = s;
-        tmax = fmaxf(tmax, s);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sacc[mb][v]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * csc;  // scale > 0 keeps the order
     const bool upd = tmax > m + 8.f;
     float alpha = 1.f;
     if (upd) {
@@ -177,13 +184,13 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(AttnArgs a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) oacc[nb][v] *= alpha;
     }
-    const float ms = (m == -INFINITY) ? 0.f : m;
+    const float nms = (m == -INFINITY) ? 0.f : -m;
     float psum = 0.f;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float p = fast_exp2(sacc[mb][v] - ms);
+        const float p = fast_exp2(__builtin_fmaf(sacc[mb][v], csc, nms));
         sacc[mb][v] = p;
         psum += p;
       }
@@ -200,16 +207,27 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(AttnArgs a) {
         pw.z = pack_bf16x2(sacc[mb][8 * kq + 4], sacc[mb][8 * kq + 5]);
         pw.w = pack_bf16x2(sacc[mb][8 * kq + 6], sacc[mb][8 * kq + 7]);
         const bf16x8 pop = as_bf16x8(pw);
+        // V^T operand: slots 0..3 are keys key0 + 0..3, slots 4..7 keys key0 + 8..11
+        const int key0 = mb * 32 + 16 * kq + 4 * half;
+        const int j16 = lane & 15;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
-          const uint16_t* vrow = &vt[(nb * 32 + l32) * kVtStride + mb * 32 + 16 * kq + 4 * half];
-          const uint2 lo4 = *reinterpret_cast<const uint2*>(vrow);
-          const uint2 hi4 = *reinterpret_cast<const uint2*>(vrow + 8);
-          const bf16x8 vop = as_bf16x8(make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
+          const uint16_t* vp = &vs[(key0 + (j16 >> 2)) * kVsStride + nb * 32 + ((lane >> 4) & 1) * 16 + 4 * (j16 & 3)];
+          const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)vp);
+          const v4s r2 =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(vp + 8 * kVsStride));
+          const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r1, r2, 0, 1, 2, 3, 4, 5, 6, 7));
           oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, oacc[nb], 0, 0, 0);
         }
       }
-  }
+  };
+
+  gather(0);
+  // tiles whose keys all lie at or before the first row's position need no mask
+  const int kt_mask = min(kv_end, ((min_pos + 1) / kKeyTile) * kKeyTile);
+  int kt = 0;
+  for (; kt < kt_mask; kt += kKeyTile) key_tile(kt, std::false_type{});
+  for (; kt < kv_end; kt += kKeyTile) key_tile(kt, std::true_type{});
 
   const float L = lsum + __shfl_xor(lsum, 32, 64);
   if (row_valid) {
