@@ -203,20 +203,28 @@ def main(argv=None):
     extend_tflops = ext_flops / (mean_ms[3] * 1e-3) / 1e12 if has_extend else None
     store_gbps = st_bytes / (mean_ms[1] * 1e-3) / 1e9
     decode_dominant = has_decode and (not has_extend or mean_ms[2] >= mean_ms[3])
+    from paged_kv_attention_08_amd import profiling
+    call = "paged_decode_attn" if decode_dominant else "paged_extend_attn"
+    measured = profiling.traffic_for(call, args.config)  # None unless taken on the current kernel sources
+    traffic = None if measured is None else round(measured["traffic_bytes"])
     if decode_dominant:
         value = (dec_bytes + st_bytes + md_bytes) / (ms_per_step * 1e-3) / 1e9
         unit = "GB/s"
         roof = {"bound": "hbm", "achieved": round(decode_gbps, 1), "peak": PM.HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(decode_gbps / PM.HBM_PEAK_GBPS, 4), "traffic": None,
+                "frac": round(decode_gbps / PM.HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "kernel": "paged_decode_attn (decode_partial_kernel + decode_merge_kernel)",
-                "algorithmic_bytes_per_launch": dec_bytes, "avg_launch_ms": round(float(mean_ms[2]), 4)}
+                "algorithmic_bytes_per_launch": dec_bytes, "avg_launch_ms": round(float(mean_ms[2]), 4),
+                "profile": None if measured is None else measured["summary"]}
     else:
         value = ext_flops / (ms_per_step * 1e-3) / 1e12
         unit = "TFLOP/s"
         roof = {"bound": "mfma", "achieved": round(extend_tflops, 1), "peak": PM.BF16_DENSE_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(extend_tflops / PM.BF16_DENSE_PEAK_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(extend_tflops / PM.BF16_DENSE_PEAK_TFLOPS, 4), "traffic": traffic,
+                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "kernel": "paged_extend_attn (extend_kernel)", "algorithmic_flops_per_launch": ext_flops,
-                "avg_launch_ms": round(float(mean_ms[3]), 4)}
+                "avg_launch_ms": round(float(mean_ms[3]), 4),
+                "profile": None if measured is None else measured["summary"]}
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
