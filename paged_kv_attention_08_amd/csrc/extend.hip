@@ -7,26 +7,33 @@
 // the matrix units busy.  Deep dive 5.2: FlashAttention tiling with an online
 // softmax keeps the n x n score matrix out of HBM.
 //
-// Work decomposition: one workgroup (4 wavefronts) per plan tile = (request,
-// TQ consecutive new tokens) and KV head g.  Its 128 rows are the
-// (token, query head) pairs of the tile that share KV head g, token-major
+// Work decomposition: one workgroup (8 wavefronts, one per 32 rows) per plan
+// tile = (request, TQ consecutive new tokens) and KV head g.  Its 256 rows are
+// the (token, query head) pairs of the tile that share KV head g, token-major
 // (row = tq * G + query head within the group), so each gathered K/V tile is
-// loaded once for all G query heads.  Wavefront w owns rows 32w..32w+31.
+// loaded once for all G query heads and 256 rows.  Wavefront w owns rows
+// 32w..32w+31.  Workgroups are dispatched round-robin over the 8 XCDs, each
+// with its own L2; the (head, tile) items are laid out so that every XCD
+// takes one contiguous, request-major range of them, and the workgroups that
+// re-read one request's K/V for one head (and a radix-shared prefix) meet in
+// the same L2.
 //
 // Per 64-key tile:
 //   * the workgroup gathers 64 K rows and 64 V rows of head g into registers
-//     one tile ahead: wavefront w takes keys 16w..16w+15, each 16-lane group
-//     one whole 256-byte head row per load (16 bytes per lane), so a load
-//     instruction touches 4 rows.  (With one key per lane, every instruction
-//     touched 64 scattered rows and half the address translations missed the
-//     per-CU TLB.)  Both tiles are stored row-major ([key][d]) in LDS as
-//     contiguous 256-byte runs;
+//     two tiles ahead (two register sets, page-table entries one tile before
+//     that): wavefront w takes keys 8w..8w+7, each 16-lane group one whole
+//     256-byte head row per load (16 bytes per lane), so a load instruction
+//     touches 4 rows.  (With one key per lane, every instruction touched 64
+//     scattered rows and half the address translations missed the per-CU
+//     TLB.)  Both tiles are stored row-major ([key][d]) in LDS as contiguous
+//     256-byte runs, in two stages: tile n + 1 is stored while tile n is in
+//     use, so one barrier per tile suffices;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys x rows): the K operand
 //     is read from LDS, Q stays in registers for the whole loop.  In the
 //     32x32 accumulator layout each lane owns one row (query) and 16 of its 32
 //     keys, so the row max needs one cross-half shuffle;
 //   * causal masking is applied only on tiles that reach past the first
-//     row's position (a separately compiled loop); prefix tiles run unmasked;
+//     row's position; prefix tiles run unmasked;
 //   * online softmax in fp32 (the max moves only when it grows by more than
 //     2^8, so the output accumulator is rarely rescaled);
 //   * O^T += V^T P^T: the probabilities, rounded to bf16, are used as the B
@@ -46,20 +53,34 @@ namespace {
 constexpr int kKeyTile = 64;
 constexpr int kKsStride = 136;  // bf16 elements per K row in LDS (128 + 8 pad)
 constexpr int kVsStride = 160;  // bf16 elements per V row in LDS (80 dwords: 4 rows x 16 dwords hit 64 distinct banks)
+constexpr int kWaves = 8;
+static_assert(kExtendRows == 32 * kWaves, "one 32-row block per wavefront");
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 
 __device__ inline bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ inline uint4 load16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-__global__ void __launch_bounds__(256, 2) extend_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t ks[kKeyTile * kKsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[kKeyTile * kVsStride];
+__global__ void __launch_bounds__(512, 1) extend_kernel(AttnArgs a) {
+  // two LDS stages: tile n lives in stage n % 2
+  __shared__ __attribute__((aligned(16))) uint16_t ks_all[2][kKeyTile * kKsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t vs_all[2][kKeyTile * kVsStride];
 
   const int32_t* header = reinterpret_cast<const int32_t*>(a.plan);
-  const int tile = blockIdx.x;
-  const int g = blockIdx.y;
-  if (tile >= header[2]) return;  // uniform for the workgroup
+  // Workgroups are dispatched to the 8 XCDs round-robin (linear id % 8) and
+  // each XCD has its own L2.  Give every XCD one contiguous range of the
+  // (KV head, tile) items, tiles request-major as the plan lists them, so the
+  // workgroups that re-read one request's K/V for one head share an L2.
+  const int n_tiles = header[2];
+  const int n_items = n_tiles * a.Hkv;
+  const int per_xcd = (n_items + 7) / 8;
+  const int xcd = blockIdx.x & 7;
+  const int slot_in_xcd = blockIdx.x >> 3;
+  if (slot_in_xcd >= per_xcd) return;  // uniform for the workgroup
+  const int item = xcd * per_xcd + slot_in_xcd;
+  if (item >= n_items) return;
+  const int g = item / n_tiles;
+  const int tile = item - g * n_tiles;
 
   const int2 tl = reinterpret_cast<const int2*>(a.plan + a.layout.tiles_off)[tile];
   const int i = tl.x;
@@ -95,29 +116,36 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(AttnArgs a) {
   const uint16_t* kbase = a.k_pool + (int64_t)g * kHeadDim + (lane & 15) * 8;
   const uint16_t* vbase = a.v_pool + (int64_t)g * kHeadDim + (lane & 15) * 8;
 
-  // loader: load u (0..3) of lane l moves 16 bytes (dims 8 (l % 16) ..) of key
-  // 16 w + 4 u + l / 16 of the tile
-  uint4 kpre[4], vpre[4];
-  auto gather = [&](int kt) {
-    // lane l fetches the entry of key kt + l; rows are then broadcast by shuffles.
-    // Keys past kv_end re-read the last valid key's row (masked, V zeroed).
-    int32_t ent = pt_row[min(kt + lane, kv_end - 1)];
-    if (ent < 0 || (int64_t)ent >= a.num_pool_rows) {
-      raise_status(a.status, PKV_STATUS_BAD_PAGE_ROW);
-      ent = 0;
-    }
+  // loader: load u (0..1) of lane l in wavefront w moves 16 bytes (dims
+  // 8 (l % 16) ..) of key 8 w + 4 u + l / 16 of the tile.  Keys past kv_end
+  // re-read the last valid key's row (masked, V zeroed).
+  uint4 kpre[2][2], vpre[2][2];  // [register set][load]
+  // page-table entries of the next tile to gather, one per load (16 lanes share one)
+  int32_t ent[2];
+  auto load_entries = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t prow = __shfl(ent, 16 * wave + 4 * u + (lane >> 4), 64);
-      kpre[u] = load16(kbase + prow * a.row_stride);
-      vpre[u] = load16(vbase + prow * a.row_stride);
-    }
+    for (int u = 0; u < 2; ++u) ent[u] = pt_row[min(kt + 8 * wave + 4 * u + (lane >> 4), kv_end - 1)];
   };
-  auto zero_tail = [&](int kt) {
+  auto gather = [&](int kt, auto set_tag) __attribute__((always_inline)) {
+    constexpr int SET = decltype(set_tag)::value;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      int32_t e = ent[u];
+      if (e < 0 || (int64_t)e >= a.num_pool_rows) {
+        raise_status(a.status, PKV_STATUS_BAD_PAGE_ROW);
+        e = 0;
+      }
+      kpre[SET][u] = load16(kbase + (int64_t)e * a.row_stride);
+      vpre[SET][u] = load16(vbase + (int64_t)e * a.row_stride);
+    }
+    load_entries(kt + kKeyTile);
+  };
+  auto zero_tail = [&](int kt, auto set_tag) __attribute__((always_inline)) {
+    constexpr int SET = decltype(set_tag)::value;
     if (kt + kKeyTile > kv_end) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (kt + 16 * wave + 4 * u + (lane >> 4) >= kv_end) vpre[u] = make_uint4(0, 0, 0, 0);
+      for (int u = 0; u < 2; ++u)
+        if (kt + 8 * wave + 4 * u + (lane >> 4) >= kv_end) vpre[SET][u] = make_uint4(0, 0, 0, 0);
     }
   };
 
@@ -130,33 +158,50 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(AttnArgs a) {
   float lsum = 0.f;
   const float csc = a.scale_log2;
   const int min_pos = c + t0;
+  // tiles whose keys all lie at or before the first row's position need no mask
+  const int kt_mask = min(kv_end, ((min_pos + 1) / kKeyTile) * kKeyTile);
 
-  // One 64-key tile.  MASK: the tile reaches past the first row's position,
-  // so keys beyond a row's own position are masked (diagonal and ragged end).
-  auto key_tile = [&](int kt, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    __syncthreads();
-    if (MASK) zero_tail(kt);
+  // tile kt from register set S into LDS stage S (a key past kv_end gets a zero V row)
+  auto store_tile = [&](int kt, auto set_tag) __attribute__((always_inline)) {
+    constexpr int S = decltype(set_tag)::value;
+    zero_tail(kt, set_tag);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int key = 16 * wave + 4 * u + (lane >> 4);
-      *reinterpret_cast<uint4*>(&ks[key * kKsStride + (lane & 15) * 8]) = kpre[u];
-      *reinterpret_cast<uint4*>(&vs[key * kVsStride + (lane & 15) * 8]) = vpre[u];
+    for (int u = 0; u < 2; ++u) {
+      const int key = 8 * wave + 4 * u + (lane >> 4);
+      *reinterpret_cast<uint4*>(&ks_all[S][key * kKsStride + (lane & 15) * 8]) = kpre[S][u];
+      *reinterpret_cast<uint4*>(&vs_all[S][key * kVsStride + (lane & 15) * 8]) = vpre[S][u];
     }
-    __syncthreads();
-    if (kt + kKeyTile < kv_end) gather(kt + kKeyTile);
+  };
+  // One 64-key tile in stage SET.  MASK: the tile reaches past the first
+  // row's position, so keys beyond a row's own position are masked (diagonal
+  // and ragged end).
+  auto key_tile = [&](int kt, auto set_tag) __attribute__((always_inline)) {
+    constexpr int SET = decltype(set_tag)::value;
+    const bool MASK = kt >= kt_mask;  // uniform
+    // the next tile goes to the other stage (last read before the previous
+    // barrier); its register set then receives the tile three ahead
+    if (kt + kKeyTile < kv_end) {
+      store_tile(kt + kKeyTile, std::integral_constant<int, SET ^ 1>{});
+      if (kt + 3 * kKeyTile < kv_end) gather(kt + 3 * kKeyTile, std::integral_constant<int, SET ^ 1>{});
+    }
+    const uint16_t* ks = ks_all[SET];
+    const uint16_t* vs = vs_all[SET];
 
-    // S^T = K Q^T : two 32-key blocks (raw scores, scale folded into exp below)
+    // S^T = K Q^T : two 32-key blocks (raw scores, scale folded into exp below);
+    // the two accumulation chains alternate and the K operands are read from
+    // LDS four MFMAs ahead
     f32x16 sacc[2];
+    auto kread = [&](int j) __attribute__((always_inline)) {
+      return as_bf16x8(*reinterpret_cast<const uint4*>(&ks[((j & 1) * 32 + l32) * kKsStride + half * 8 + 16 * (j >> 1)]));
+    };
+    bf16x8 kb[4];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int j = 0; j < 4; ++j) kb[j] = kread(j);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) sacc[mb][v] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const bf16x8 kop = as_bf16x8(*reinterpret_cast<const uint4*>(&ks[(mb * 32 + l32) * kKsStride + half * 8 + 16 * kk]));
-        sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[kk], sacc[mb], 0, 0, 0);
-      }
+    for (int j = 0; j < 16; ++j) {
+      const int mb = j & 1, kk = j >> 1;
+      sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[j & 3], qop[kk], kk == 0 ? f32x16{} : sacc[mb], 0, 0, 0);
+      if (j + 4 < 16) kb[j & 3] = kread(j + 4);
     }
     // element v of block mb is key kt + 32 mb + 8 (v / 4) + 4 half + v % 4 of row l32
     if (MASK) {
@@ -222,12 +267,20 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(AttnArgs a) {
       }
   };
 
-  gather(0);
-  // tiles whose keys all lie at or before the first row's position need no mask
-  const int kt_mask = min(kv_end, ((min_pos + 1) / kKeyTile) * kKeyTile);
-  int kt = 0;
-  for (; kt < kt_mask; kt += kKeyTile) key_tile(kt, std::false_type{});
-  for (; kt < kv_end; kt += kKeyTile) key_tile(kt, std::true_type{});
+  load_entries(0);
+  gather(0, std::integral_constant<int, 0>{});
+  if (kKeyTile < kv_end) gather(kKeyTile, std::integral_constant<int, 1>{});
+  store_tile(0, std::integral_constant<int, 0>{});
+  if (2 * kKeyTile < kv_end) gather(2 * kKeyTile, std::integral_constant<int, 0>{});
+  __syncthreads();
+  for (int kt = 0; kt < kv_end; kt += 2 * kKeyTile) {
+    key_tile(kt, std::integral_constant<int, 0>{});
+    __syncthreads();
+    if (kt + kKeyTile < kv_end) {
+      key_tile(kt + kKeyTile, std::integral_constant<int, 1>{});
+      __syncthreads();
+    }
+  }
 
   const float L = lsum + __shfl_xor(lsum, 32, 64);
   if (row_valid) {
@@ -250,8 +303,10 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(AttnArgs a) {
 
 hipError_t launch_extend(const AttnArgs& a, hipStream_t s) {
   if (a.num_decode >= a.B) return hipSuccess;
-  const dim3 grid((unsigned)a.layout.cap_tiles, (unsigned)a.Hkv);
-  hipLaunchKernelGGL(extend_kernel, grid, dim3(256), 0, s, a);
+  // one workgroup per (KV head, tile) item, rounded up to whole XCD rounds
+  const int64_t n = ((int64_t)a.layout.cap_tiles * a.Hkv + 7) / 8 * 8;
+  const dim3 grid((unsigned)n);
+  hipLaunchKernelGGL(extend_kernel, grid, dim3(64 * kWaves), 0, s, a);
   return hipGetLastError();
 }
 

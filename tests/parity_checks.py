@@ -15,13 +15,15 @@ MAX_ABS_TOL = 2e-2
 MEAN_ABS_TOL = 2e-3
 
 
-def sample_tokens(w, per_request: int = 12, seed: int = 0, tile_q: int = 32):
-    """Chunk offsets to check per extend request: both ends, tile edges, random."""
+def sample_tokens(w, per_request: int = 12, seed: int = 0):
+    """Chunk offsets to check per extend request: both ends, the edges of
+    tiles of 16..256 tokens, random."""
     rng = np.random.default_rng(seed)
     out = {}
     for i in range(w.num_decode, w.num_reqs):
         ext = int(w.device_len[i] - w.cached_len[i])
-        cand = {0, 1, ext - 1, ext - 2, tile_q - 1, tile_q, ext // 2}
+        cand = {0, 1, ext - 1, ext - 2, ext // 2}
+        cand |= {e + d for e in (16, 32, 64, 128, 256) for d in (-1, 0)}
         cand |= set(int(x) for x in rng.integers(0, ext, size=per_request))
         out[i] = sorted(t for t in cand if 0 <= t < ext)
     return out
