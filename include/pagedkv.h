@@ -72,7 +72,7 @@ typedef struct pkv_kv_pool {
   void*   k;             /* bf16 K rows */
   void*   v;             /* bf16 V rows */
   int64_t num_rows;      /* rows in the pool; a multiple of page_size, < 2^31 */
-  int64_t row_stride;    /* bf16 elements from one row to the next; >= num_kv_heads*head_dim, multiple of 8 */
+  int64_t row_stride;    /* bf16 elements from one row to the next; >= num_kv_heads*head_dim, multiple of 8, < 2^31 */
   int32_t page_size;     /* 1, 2, 4, ..., 64 */
   int32_t num_kv_heads;  /* Hkv */
   int32_t head_dim;      /* d; must be 128 */

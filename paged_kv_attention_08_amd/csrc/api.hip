@@ -38,7 +38,9 @@ int check_pool(const pkv_kv_pool* p) {
   if (p->num_kv_heads <= 0 || p->reserved != 0) return PKV_ERR_INVALID_ARGUMENT;
   if (p->num_rows <= 0 || p->num_rows >= (int64_t(1) << 31) || p->num_rows % p->page_size != 0)
     return PKV_ERR_INVALID_ARGUMENT;
-  if (p->row_stride < (int64_t)p->num_kv_heads * p->head_dim || p->row_stride % 8 != 0) return PKV_ERR_INVALID_ARGUMENT;
+  if (p->row_stride < (int64_t)p->num_kv_heads * p->head_dim || p->row_stride % 8 != 0 ||
+      p->row_stride >= (int64_t(1) << 31))
+    return PKV_ERR_INVALID_ARGUMENT;
   if (!aligned16(p->k) || !aligned16(p->v)) return PKV_ERR_INVALID_ARGUMENT;
   return PKV_OK;
 }

@@ -60,6 +60,10 @@ typedef short v4s __attribute__((ext_vector_type(4)));
 
 __device__ inline bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ inline uint4 load16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+__device__ inline float dot2_bf16(uint32_t w, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w), __builtin_bit_cast(bf16x2v, 0x3F803F80u), acc, false);
+}
 
 __global__ void __launch_bounds__(512, 1) extend_kernel(AttnArgs a) {
   // two LDS stages: tile n lives in stage n % 2
@@ -115,6 +119,8 @@ __global__ void __launch_bounds__(512, 1) extend_kernel(AttnArgs a) {
   const int32_t* pt_row = a.page_table + (int64_t)a.table_idx[i] * a.W;
   const uint16_t* kbase = a.k_pool + (int64_t)g * kHeadDim + (lane & 15) * 8;
   const uint16_t* vbase = a.v_pool + (int64_t)g * kHeadDim + (lane & 15) * 8;
+  const uint32_t row_elems = (uint32_t)a.row_stride;  // < 2^31, checked on the host
+  const uint32_t n_rows = (uint32_t)a.num_pool_rows;
 
   // loader: load u (0..1) of lane l in wavefront w moves 16 bytes (dims
   // 8 (l % 16) ..) of key 8 w + 4 u + l / 16 of the tile.  Keys past kv_end
@@ -128,17 +134,20 @@ __global__ void __launch_bounds__(512, 1) extend_kernel(AttnArgs a) {
   };
   auto gather = [&](int kt, auto set_tag) __attribute__((always_inline)) {
     constexpr int SET = decltype(set_tag)::value;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      int32_t e = ent[u];
-      if (e < 0 || (int64_t)e >= a.num_pool_rows) {
-        raise_status(a.status, PKV_STATUS_BAD_PAGE_ROW);
-        e = 0;
-      }
-      kpre[SET][u] = load16(kbase + (int64_t)e * a.row_stride);
-      vpre[SET][u] = load16(vbase + (int64_t)e * a.row_stride);
-    }
+    uint32_t r0 = (uint32_t)ent[0], r1 = (uint32_t)ent[1];
+    const bool b0 = r0 >= n_rows, b1 = r1 >= n_rows;  // also catches negative entries
+    r0 = b0 ? 0u : r0;
+    r1 = b1 ? 0u : r1;
+    // the next tile's entries are requested before this tile's rows, so the
+    // wait for them (one tile later) can leave these row loads in flight
     load_entries(kt + kKeyTile);
+    // 32 x 32 -> 64-bit row offsets
+    const uint64_t off0 = (uint64_t)r0 * row_elems, off1 = (uint64_t)r1 * row_elems;
+    kpre[SET][0] = load16(kbase + off0);
+    vpre[SET][0] = load16(vbase + off0);
+    kpre[SET][1] = load16(kbase + off1);
+    vpre[SET][1] = load16(vbase + off1);
+    if (b0 || b1) raise_status(a.status, PKV_STATUS_BAD_PAGE_ROW);
   };
   auto zero_tail = [&](int kt, auto set_tag) __attribute__((always_inline)) {
     constexpr int SET = decltype(set_tag)::value;
@@ -230,16 +239,11 @@ __global__ void __launch_bounds__(512, 1) extend_kernel(AttnArgs a) {
         for (int v = 0; v < 16; ++v) oacc[nb][v] *= alpha;
     }
     const float nms = (m == -INFINITY) ? 0.f : -m;
-    float psum = 0.f;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = fast_exp2(__builtin_fmaf(sacc[mb][v], csc, nms));
-        sacc[mb][v] = p;
-        psum += p;
-      }
-    lsum = lsum * alpha + psum;
+      for (int v = 0; v < 16; ++v) sacc[mb][v] = fast_exp2(__builtin_fmaf(sacc[mb][v], csc, nms));
+    float psum0 = 0.f, psum1 = 0.f;
 
     // O^T += V^T P^T, 16 keys per MFMA
 #pragma unroll
@@ -251,6 +255,10 @@ __global__ void __launch_bounds__(512, 1) extend_kernel(AttnArgs a) {
         pw.y = pack_bf16x2(sacc[mb][8 * kq + 2], sacc[mb][8 * kq + 3]);
         pw.z = pack_bf16x2(sacc[mb][8 * kq + 4], sacc[mb][8 * kq + 5]);
         pw.w = pack_bf16x2(sacc[mb][8 * kq + 6], sacc[mb][8 * kq + 7]);
+        psum0 = dot2_bf16(pw.x, psum0);
+        psum1 = dot2_bf16(pw.y, psum1);
+        psum0 = dot2_bf16(pw.z, psum0);
+        psum1 = dot2_bf16(pw.w, psum1);
         const bf16x8 pop = as_bf16x8(pw);
         // V^T operand: slots 0..3 are keys key0 + 0..3, slots 4..7 keys key0 + 8..11
         const int key0 = mb * 32 + 16 * kq + 4 * half;
@@ -265,6 +273,7 @@ __global__ void __launch_bounds__(512, 1) extend_kernel(AttnArgs a) {
           oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, oacc[nb], 0, 0, 0);
         }
       }
+    lsum = lsum * alpha + (psum0 + psum1);
   };
 
   load_entries(0);

@@ -98,6 +98,7 @@ B = ctypes.byref
     (dict(num_rows=1 << 31), _lib.PKV_ERR_INVALID_ARGUMENT),
     (dict(row_stride=1000), _lib.PKV_ERR_INVALID_ARGUMENT),
     (dict(row_stride=1028), _lib.PKV_ERR_INVALID_ARGUMENT),
+    (dict(row_stride=1 << 31), _lib.PKV_ERR_INVALID_ARGUMENT),
     (dict(reserved=1), _lib.PKV_ERR_INVALID_ARGUMENT),
     (dict(k=FAKE + 2), _lib.PKV_ERR_INVALID_ARGUMENT),
 ])
