@@ -12,6 +12,9 @@
  *   kv_store             scatter of the new K/V rows to their out_loc rows
  *   paged_decode_attn    split-K decode attention (one new token per request)
  *   paged_extend_attn    chunked-prefill attention on a cached prefix
+ *   kv_store_rope        kv_store with rotary position embedding (and an
+ *                        optional per-head RMS norm) applied to q and k on
+ *                        the way (deep dive sections 7.2-7.3)
  *
  * Conventions shared by every entry point
  *   - Every pointer inside the structs and every data argument is a DEVICE
@@ -60,6 +63,7 @@ extern "C" {
 #define PKV_STATUS_BAD_DECODE     0x10  /* a request below num_decode whose extend_len != 1: skipped */
 #define PKV_STATUS_TOKEN_COUNT    0x20  /* sum of extend_len differs from num_tokens */
 #define PKV_STATUS_BAD_ALLOC      0x40  /* alloc_rows entry misaligned, outside the pool, or too few entries */
+#define PKV_STATUS_BAD_POSITION   0x80  /* positions[t] outside [0, max_position): token skipped by kv_store_rope */
 
 /* ---- data structures ---------------------------------------------------- */
 
@@ -200,6 +204,53 @@ int paged_decode_attn(const pkv_kv_pool* pool, const pkv_page_table* page_table,
 int paged_extend_attn(const pkv_kv_pool* pool, const pkv_page_table* page_table, const pkv_batch* batch,
                       const pkv_attn_metadata* meta, const void* q, void* o, int32_t num_qo_heads,
                       float sm_scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- rotary position embedding fused into the store ----------------------- */
+
+/* Optional RMS norm of every q and k head row before the rotation (deep dive
+ * 7.2: models such as Qwen3 normalise q and k per head):
+ *   x <- x / sqrt(mean(x^2) + eps) * weight, over the head_dim elements.
+ * The normalised row is rotated without an intermediate bf16 rounding. */
+typedef struct pkv_qk_norm {
+  const void* q_weight;  /* bf16 [head_dim] */
+  const void* k_weight;  /* bf16 [head_dim] */
+  float eps;             /* >= 0 */
+  int32_t reserved;      /* must be 0 */
+} pkv_qk_norm;
+
+/* pkv_rope_cos_sin_cache: the rotary table of deep dive 7.3 (rotary_dim equal
+ * to head_dim, inverse frequencies theta_i = base^(-2i/head_dim)):
+ *   cache[p * head_dim + i]              = cos(p * theta_i)
+ *   cache[p * head_dim + head_dim/2 + i] = sin(p * theta_i)
+ * for p < max_position and i < head_dim/2.  Angles are formed in float64 and
+ * the values rounded to float.
+ *   cache : float [max_position, head_dim], caller-owned, 16-byte aligned
+ * Built once per model; head_dim must be 128, base > 1. */
+int pkv_rope_cos_sin_cache(float* cache, int32_t max_position, int32_t head_dim, double base, void* stream);
+
+/* kv_store_rope: for each token t < num_tokens with p = positions[t]
+ * (deep dive 7.2-7.3: the attention layer rotates q and k by position, then
+ * the backend stores K/V):
+ *   every q head row and k head row x (optionally RMS-normed first) becomes
+ *     y_j          = x_j * cos(p theta_j) - x_{j+d/2} * sin(p theta_j)
+ *     y_{j+d/2}    = x_{j+d/2} * cos(p theta_j) + x_j * sin(p theta_j)
+ *   (the "rotate half" pairing, j < d/2, cos/sin read from the table);
+ *   q is rotated in place, the rotated k goes to K[out_loc[t]] and v_new[t]
+ *   to V[out_loc[t]] unchanged.
+ *   q            : bf16 [num_tokens, num_qo_heads, head_dim], in/out
+ *   k_new, v_new : bf16 [num_tokens, Hkv, head_dim]
+ *   out_loc, positions : int32 [num_tokens] (positions as build_attn_metadata writes them)
+ *   cos_sin_cache : float [max_position, head_dim] from pkv_rope_cos_sin_cache
+ *   qk_norm      : NULL for no norm (host struct, device weights)
+ * All rows 16-byte aligned and contiguous.  A token whose position is outside
+ * [0, max_position) is left entirely untouched (PKV_STATUS_BAD_POSITION); one
+ * whose out_loc is outside the pool has q rotated but nothing stored
+ * (PKV_STATUS_BAD_OUT_LOC).  Tokens sharing a target row race as in kv_store.
+ * num_tokens == 0 is a no-op. */
+int kv_store_rope(const pkv_kv_pool* pool, void* q, int32_t num_qo_heads, const void* k_new, const void* v_new,
+                  const int32_t* out_loc, const int32_t* positions, int64_t num_tokens,
+                  const float* cos_sin_cache, int32_t max_position, const pkv_qk_norm* qk_norm,
+                  int32_t* status, void* stream);
 
 /* ---- diagnostics -------------------------------------------------------- */
 const char* pkv_error_string(int code);   /* static string, never NULL */

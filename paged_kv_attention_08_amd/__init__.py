@@ -19,10 +19,12 @@ import torch
 
 from . import _lib
 from ._lib import (PKV_STATUS_BAD_ALLOC, PKV_STATUS_BAD_DECODE, PKV_STATUS_BAD_LENGTHS, PKV_STATUS_BAD_OUT_LOC,
-                   PKV_STATUS_BAD_PAGE_ROW, PKV_STATUS_BAD_TABLE_IDX, PKV_STATUS_TOKEN_COUNT)
+                   PKV_STATUS_BAD_PAGE_ROW, PKV_STATUS_BAD_POSITION, PKV_STATUS_BAD_TABLE_IDX,
+                   PKV_STATUS_TOKEN_COUNT)
 
 __all__ = ["PagedKVError", "KVPoolTensors", "BatchTensors", "MetadataBuffers", "kv_store", "build_attn_metadata",
            "paged_decode_attn", "paged_extend_attn", "plan_bytes", "workspace_bytes", "library_path",
+           "rope_cos_sin_cache", "kv_store_rope", "PKV_STATUS_BAD_POSITION",
            "PKV_STATUS_BAD_ALLOC", "PKV_STATUS_BAD_DECODE", "PKV_STATUS_BAD_LENGTHS", "PKV_STATUS_BAD_OUT_LOC",
            "PKV_STATUS_BAD_PAGE_ROW", "PKV_STATUS_BAD_TABLE_IDX", "PKV_STATUS_TOKEN_COUNT"]
 
@@ -50,7 +52,7 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _need(t: torch.Tensor, name: str, dtype, dims=None):
+def _need(t: torch.Tensor, name: str, dtype, dims=None, contiguous: bool = True):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a tensor")
     if not t.is_cuda:
@@ -59,7 +61,7 @@ def _need(t: torch.Tensor, name: str, dtype, dims=None):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if dims is not None and t.dim() != dims:
         raise ValueError(f"{name} must have {dims} dims, got shape {tuple(t.shape)}")
-    if not t.is_contiguous():
+    if contiguous and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
 
 
@@ -70,18 +72,22 @@ def _check(fn: str, code: int):
 
 @dataclass
 class KVPoolTensors:
-    """One layer's pool: k and v are bf16 [num_rows, Hkv, d]."""
+    """One layer's pool: k and v are bf16 [num_rows, Hkv, d] views whose rows
+    may be further apart than Hkv * d elements (e.g. one layer of a pool that
+    interleaves layers), with each row's heads contiguous."""
     k: torch.Tensor
     v: torch.Tensor
     page_size: int = 1
 
     def struct(self) -> _lib.KVPool:
-        _need(self.k, "k_pool", torch.bfloat16, 3)
-        _need(self.v, "v_pool", torch.bfloat16, 3)
-        if self.k.shape != self.v.shape:
-            raise ValueError("k and v pools differ in shape")
+        _need(self.k, "k_pool", torch.bfloat16, 3, contiguous=False)
+        _need(self.v, "v_pool", torch.bfloat16, 3, contiguous=False)
+        if self.k.shape != self.v.shape or self.k.stride() != self.v.stride():
+            raise ValueError("k and v pools differ in shape or strides")
         n, hkv, d = self.k.shape
-        return _lib.KVPool(self.k.data_ptr(), self.v.data_ptr(), n, hkv * d, self.page_size, hkv, d, 0)
+        if self.k.stride(2) != 1 or self.k.stride(1) != d:
+            raise ValueError("each pool row's heads must be contiguous")
+        return _lib.KVPool(self.k.data_ptr(), self.v.data_ptr(), n, self.k.stride(0), self.page_size, hkv, d, 0)
 
 
 @dataclass
@@ -208,3 +214,48 @@ def paged_extend_attn(pool: KVPoolTensors, page_table: torch.Tensor, batch: Batc
                       q: torch.Tensor, o: torch.Tensor, sm_scale: float, workspace: Optional[torch.Tensor] = None,
                       stream=None) -> None:
     _attn("paged_extend_attn", pool, page_table, batch, meta, q, o, sm_scale, workspace, stream)
+
+
+def rope_cos_sin_cache(cache: torch.Tensor, base: float, stream=None) -> None:
+    """Fill cache (float32 [max_position, head_dim]) with the rotary table:
+    cos(p theta_i) in the first half of row p, sin(p theta_i) in the second,
+    theta_i = base^(-2i/head_dim)."""
+    _need(cache, "cache", torch.float32, 2)
+    if not cache.is_contiguous():
+        raise ValueError("cache must be contiguous")
+    _check("pkv_rope_cos_sin_cache", _lib.lib().pkv_rope_cos_sin_cache(cache.data_ptr(), cache.shape[0],
+                                                                       cache.shape[1], float(base), _stream(stream)))
+
+
+def kv_store_rope(pool: KVPoolTensors, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                  out_loc: torch.Tensor, positions: torch.Tensor, cos_sin_cache: torch.Tensor,
+                  qk_norm: Optional[tuple] = None, status: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Rotate q in place and k by positions (after the optional per-head RMS
+    norm qk_norm = (q_weight, k_weight, eps)), then store k and v at out_loc."""
+    p = pool.struct()
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_new, "k_new", torch.bfloat16, 3)
+    _need(v_new, "v_new", torch.bfloat16, 3)
+    _need(out_loc, "out_loc", torch.int32, 1)
+    _need(positions, "positions", torch.int32, 1)
+    _need(cos_sin_cache, "cos_sin_cache", torch.float32, 2)
+    t = k_new.shape[0]
+    if (v_new.shape != k_new.shape or k_new.shape[1:] != pool.k.shape[1:] or q.shape[0] < t
+            or q.shape[2] != pool.k.shape[2] or out_loc.numel() < t or positions.numel() < t
+            or cos_sin_cache.shape[1] != pool.k.shape[2]):
+        raise ValueError("q / k_new / v_new / out_loc / positions / cache shapes do not match the pool")
+    for name, x in (("q", q), ("k_new", k_new), ("v_new", v_new), ("cos_sin_cache", cos_sin_cache)):
+        if not x.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    norm = None
+    if qk_norm is not None:
+        qw, kw, eps = qk_norm
+        _need(qw, "q_weight", torch.bfloat16, 1)
+        _need(kw, "k_weight", torch.bfloat16, 1)
+        norm = _lib.QKNorm(qw.data_ptr(), kw.data_ptr(), float(eps), 0)
+    if status is not None:
+        _need(status, "status", torch.int32, 1)
+    _check("kv_store_rope", _lib.lib().kv_store_rope(
+        ctypes.byref(p), q.data_ptr(), q.shape[1], k_new.data_ptr(), v_new.data_ptr(), out_loc.data_ptr(),
+        positions.data_ptr(), t, cos_sin_cache.data_ptr(), cos_sin_cache.shape[0],
+        ctypes.byref(norm) if norm is not None else None, _ptr(status), _stream(stream)))

@@ -22,6 +22,7 @@ PKV_STATUS_BAD_PAGE_ROW = 0x08
 PKV_STATUS_BAD_DECODE = 0x10
 PKV_STATUS_TOKEN_COUNT = 0x20
 PKV_STATUS_BAD_ALLOC = 0x40
+PKV_STATUS_BAD_POSITION = 0x80
 
 
 class KVPool(ctypes.Structure):
@@ -44,6 +45,10 @@ class AttnMetadata(ctypes.Structure):
                 ("plan_bytes", c_size_t), ("status", c_void_p)]
 
 
+class QKNorm(ctypes.Structure):
+    _fields_ = [("q_weight", c_void_p), ("k_weight", c_void_p), ("eps", c_float), ("reserved", c_int32)]
+
+
 # name -> (restype, argtypes); the exports of include/pagedkv.h
 PROTOTYPES = {
     "pkv_plan_bytes": (c_size_t, [c_int32, c_int64, c_int32, c_int32]),
@@ -55,6 +60,9 @@ PROTOTYPES = {
                                   c_void_p, c_void_p, c_int32, c_float, c_void_p, c_size_t, c_void_p]),
     "paged_extend_attn": (c_int, [POINTER(KVPool), POINTER(PageTable), POINTER(Batch), POINTER(AttnMetadata),
                                   c_void_p, c_void_p, c_int32, c_float, c_void_p, c_size_t, c_void_p]),
+    "pkv_rope_cos_sin_cache": (c_int, [c_void_p, c_int32, c_int32, ctypes.c_double, c_void_p]),
+    "kv_store_rope": (c_int, [POINTER(KVPool), c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int64,
+                              c_void_p, c_int32, POINTER(QKNorm), c_void_p, c_void_p]),
     "pkv_error_string": (ctypes.c_char_p, [c_int]),
     "pkv_last_hip_error": (c_int, []),
     "pkv_version": (c_int, []),

@@ -1,6 +1,6 @@
 // extern "C" entry points: host-side argument checks, then launches on the
 // caller's stream.  Nothing here allocates, frees or synchronises.
-#include <math.h>
+#include <cmath>
 
 #include "kernels.hpp"
 
@@ -75,7 +75,7 @@ int fill_attn_args(const pkv_kv_pool* pool, const pkv_page_table* pt, const pkv_
   if ((rc = check_page_table(pt)) != PKV_OK) return rc;
   if ((rc = check_batch(batch)) != PKV_OK) return rc;
   if ((rc = check_heads(hq, pool->num_kv_heads)) != PKV_OK) return rc;
-  if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return PKV_ERR_INVALID_ARGUMENT;
+  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return PKV_ERR_INVALID_ARGUMENT;
   if (batch->num_tokens > 0 && (!q || !o || !aligned16(q) || !aligned16(o))) return PKV_ERR_INVALID_ARGUMENT;
   PlanLayout L;
   if ((rc = check_meta_common(meta, batch, hq / pool->num_kv_heads, pool->num_kv_heads, &L)) != PKV_OK) return rc;
@@ -216,6 +216,55 @@ int paged_extend_attn(const pkv_kv_pool* pool, const pkv_page_table* page_table,
   if (rc != PKV_OK) return rc;
   if (batch->num_decode >= batch->num_reqs) return PKV_OK;
   hipError_t e = launch_extend(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : hip_failed(e);
+}
+
+int pkv_rope_cos_sin_cache(float* cache, int32_t max_position, int32_t head_dim, double base, void* stream) {
+  if (!cache || !aligned16(cache) || max_position <= 0) return PKV_ERR_INVALID_ARGUMENT;
+  if (head_dim != kHeadDim) return PKV_ERR_UNSUPPORTED;
+  if (!(base > 1.0) || !std::isfinite(base)) return PKV_ERR_INVALID_ARGUMENT;
+  RopeCacheArgs a;
+  a.cache = cache;
+  a.max_position = max_position;
+  a.log2_base = std::log2(base);
+  hipError_t e = launch_rope_cache(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : hip_failed(e);
+}
+
+int kv_store_rope(const pkv_kv_pool* pool, void* q, int32_t num_qo_heads, const void* k_new, const void* v_new,
+                  const int32_t* out_loc, const int32_t* positions, int64_t num_tokens,
+                  const float* cos_sin_cache, int32_t max_position, const pkv_qk_norm* qk_norm,
+                  int32_t* status, void* stream) {
+  int rc = check_pool(pool);
+  if (rc != PKV_OK) return rc;
+  if (num_tokens < 0 || num_qo_heads <= 0 || num_qo_heads % pool->num_kv_heads != 0) return PKV_ERR_INVALID_ARGUMENT;
+  if (max_position <= 0 || !cos_sin_cache || !aligned16(cos_sin_cache)) return PKV_ERR_INVALID_ARGUMENT;
+  if (qk_norm && (!qk_norm->q_weight || !qk_norm->k_weight || !aligned16(qk_norm->q_weight) ||
+                  !aligned16(qk_norm->k_weight) || !(qk_norm->eps >= 0.f) || qk_norm->reserved != 0))
+    return PKV_ERR_INVALID_ARGUMENT;
+  if (num_tokens == 0) return PKV_OK;
+  if (!q || !k_new || !v_new || !out_loc || !positions || !aligned16(q) || !aligned16(k_new) || !aligned16(v_new))
+    return PKV_ERR_INVALID_ARGUMENT;
+  RopeArgs a;
+  a.q = static_cast<uint16_t*>(q);
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.out_loc = out_loc;
+  a.positions = positions;
+  a.cos_sin = cos_sin_cache;
+  a.q_weight = qk_norm ? static_cast<const uint16_t*>(qk_norm->q_weight) : nullptr;
+  a.k_weight = qk_norm ? static_cast<const uint16_t*>(qk_norm->k_weight) : nullptr;
+  a.eps = qk_norm ? qk_norm->eps : 0.f;
+  a.k_pool = static_cast<uint16_t*>(pool->k);
+  a.v_pool = static_cast<uint16_t*>(pool->v);
+  a.num_tokens = num_tokens;
+  a.row_stride = pool->row_stride;
+  a.num_rows = pool->num_rows;
+  a.Hq = num_qo_heads;
+  a.Hkv = pool->num_kv_heads;
+  a.max_position = max_position;
+  a.status = status;
+  hipError_t e = launch_kv_store_rope(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : hip_failed(e);
 }
 

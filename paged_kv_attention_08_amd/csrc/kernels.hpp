@@ -18,6 +18,31 @@ struct StoreArgs {
   int32_t* status;
 };
 
+struct RopeArgs {
+  uint16_t* q;                // [T, Hq, 128], rotated in place
+  const uint16_t* k_new;      // [T, Hkv, 128]
+  const uint16_t* v_new;      // [T, Hkv, 128]
+  const int32_t* out_loc;
+  const int32_t* positions;
+  const float* cos_sin;       // [max_position, 128]
+  const uint16_t* q_weight;   // bf16 [128] or null (no norm)
+  const uint16_t* k_weight;
+  float eps;
+  uint16_t* k_pool;
+  uint16_t* v_pool;
+  int64_t num_tokens;
+  int64_t row_stride;         // elements between pool rows
+  int64_t num_rows;
+  int32_t Hq, Hkv, max_position;
+  int32_t* status;
+};
+
+struct RopeCacheArgs {
+  float* cache;
+  int32_t max_position;
+  double log2_base;
+};
+
 struct MetaArgs {
   int32_t B, num_decode, R, W, page_shift, group;
   int64_t T, num_pool_rows, num_alloc;
@@ -61,6 +86,8 @@ struct AttnArgs {
 };
 
 hipError_t launch_kv_store(const StoreArgs& a, hipStream_t s);
+hipError_t launch_kv_store_rope(const RopeArgs& a, hipStream_t s);
+hipError_t launch_rope_cache(const RopeCacheArgs& a, hipStream_t s);
 hipError_t launch_metadata(const MetaArgs& a, hipStream_t s);
 hipError_t launch_decode(const AttnArgs& a, hipStream_t s);
 hipError_t launch_extend(const AttnArgs& a, hipStream_t s);

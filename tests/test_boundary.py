@@ -175,3 +175,44 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_LIB", None)
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         _lib.lib()
+
+
+def _rope_call(lib, pool_kw=None, q=FAKE, hq=32, k=FAKE, v=FAKE, out_loc=FAKE, positions=FAKE, t=4, cache=FAKE,
+               max_pos=4096, norm=None):
+    p = pool(**(pool_kw or {}))
+    return lib.kv_store_rope(ctypes.byref(p), q, hq, k, v, out_loc, positions, t, cache, max_pos,
+                             ctypes.byref(norm) if norm is not None else None, None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(pool_kw=dict(head_dim=64)), _lib.PKV_ERR_UNSUPPORTED),
+    (dict(hq=0), _lib.PKV_ERR_INVALID_ARGUMENT),
+    (dict(hq=12), _lib.PKV_ERR_INVALID_ARGUMENT),       # not a multiple of Hkv = 8
+    (dict(t=-1), _lib.PKV_ERR_INVALID_ARGUMENT),
+    (dict(cache=None), _lib.PKV_ERR_INVALID_ARGUMENT),
+    (dict(cache=FAKE + 4), _lib.PKV_ERR_INVALID_ARGUMENT),
+    (dict(max_pos=0), _lib.PKV_ERR_INVALID_ARGUMENT),
+    (dict(q=None), _lib.PKV_ERR_INVALID_ARGUMENT),
+    (dict(q=FAKE + 8), _lib.PKV_ERR_INVALID_ARGUMENT),
+    (dict(positions=None), _lib.PKV_ERR_INVALID_ARGUMENT),
+    (dict(out_loc=None), _lib.PKV_ERR_INVALID_ARGUMENT),
+    (dict(norm=_lib.QKNorm(None, FAKE, 1e-6, 0)), _lib.PKV_ERR_INVALID_ARGUMENT),
+    (dict(norm=_lib.QKNorm(FAKE, FAKE, -1.0, 0)), _lib.PKV_ERR_INVALID_ARGUMENT),
+    (dict(norm=_lib.QKNorm(FAKE, FAKE, float("nan"), 0)), _lib.PKV_ERR_INVALID_ARGUMENT),
+    (dict(norm=_lib.QKNorm(FAKE, FAKE, 1e-6, 1)), _lib.PKV_ERR_INVALID_ARGUMENT),
+    (dict(t=0), _lib.PKV_OK),                             # nothing to do: returns before any launch
+])
+def test_kv_store_rope_rejects(lib, kw, code):
+    assert _rope_call(lib, **kw) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, 4096, 128, 1e4), _lib.PKV_ERR_INVALID_ARGUMENT),
+    ((FAKE + 4, 4096, 128, 1e4), _lib.PKV_ERR_INVALID_ARGUMENT),
+    ((FAKE, 0, 128, 1e4), _lib.PKV_ERR_INVALID_ARGUMENT),
+    ((FAKE, 4096, 64, 1e4), _lib.PKV_ERR_UNSUPPORTED),
+    ((FAKE, 4096, 128, 1.0), _lib.PKV_ERR_INVALID_ARGUMENT),
+    ((FAKE, 4096, 128, float("inf")), _lib.PKV_ERR_INVALID_ARGUMENT),
+])
+def test_rope_cache_rejects(lib, args, code):
+    assert lib.pkv_rope_cos_sin_cache(*args, None) == code

@@ -1,0 +1,152 @@
+"""GPU parity of the fused RoPE store (kv_store_rope) and its rotary table
+against the fp64 oracle (oracle/rope_oracle.py), through the C ABI.
+
+Bar: V rows bit-exact; rotated q and k within one bf16 ulp of the unrounded
+oracle value plus 1e-6 of the row's largest magnitude (fp32 rotation and norm
+before the bf16 rounding); table values within 1.2e-7 (float rounding of
+float64 cos/sin)."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_attention_08_amd as pkv
+import oracle.rope_oracle as R
+from oracle.pagedkv_oracle import widen_bf16
+from tests.gpu_harness import bf16_tensor, i32, log
+from workloads.rope_inputs import NORM_EPS, rope_inputs
+
+pytestmark = pytest.mark.gpu
+D = 128
+
+
+def ulp_bf16(x):
+    a = np.maximum(np.abs(x), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(a)) - 7)
+
+
+def assert_rows_close(got_bits, want, what):
+    got = widen_bf16(got_bits)
+    scale = np.max(np.abs(want), axis=-1, keepdims=True)
+    err = np.abs(got - want)
+    tol = ulp_bf16(want) + 1e-6 * scale
+    bad = err > tol
+    assert not bad.any(), f"{what}: {bad.sum()} elements off, worst {err[bad].max() if bad.any() else 0}"
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def make_cache(max_pos, base):
+    cache = torch.empty((max_pos, D), dtype=torch.float32, device="cuda")
+    pkv.rope_cos_sin_cache(cache, base)
+    return cache
+
+
+@pytest.mark.parametrize("base", [1e4, 1e6])
+def test_rope_table(base):
+    max_pos = 131072
+    log(f"rope table base {base} max_position {max_pos}")
+    cache = make_cache(max_pos, base).cpu().numpy().astype(np.float64)
+    f = R.inv_freq(D, base)
+    rows = np.r_[0, 1, 2, 4095, 4096, 65535, max_pos - 1, np.random.default_rng(0).integers(0, max_pos, 200)]
+    ang = rows[:, None].astype(np.float64) * f[None, :]
+    assert np.abs(cache[rows, : D // 2] - np.cos(ang)).max() <= 1.2e-7
+    assert np.abs(cache[rows, D // 2:] - np.sin(ang)).max() <= 1.2e-7
+
+
+def run_rope(inp, hq, hkv, base, norm, row_stride=None):
+    dev = "cuda"
+    N = inp.num_pool_rows
+    stride = row_stride or hkv * D
+    k_store = torch.zeros((N, stride), dtype=torch.bfloat16, device=dev)
+    v_store = torch.zeros((N, stride), dtype=torch.bfloat16, device=dev)
+    k_pool = torch.as_strided(k_store, (N, hkv, D), (stride, D, 1))
+    v_pool = torch.as_strided(v_store, (N, hkv, D), (stride, D, 1))
+    pool = pkv.KVPoolTensors(k_pool, v_pool, page_size=1)
+    q = bf16_tensor(inp.q, dev)
+    k = bf16_tensor(inp.k, dev)
+    v = bf16_tensor(inp.v, dev)
+    cache = make_cache(inp.max_position, base)
+    qk = None
+    if norm:
+        qk = (bf16_tensor(inp.q_weight, dev), bf16_tensor(inp.k_weight, dev), NORM_EPS)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    pkv.kv_store_rope(pool, q, k, v, i32(inp.out_loc, dev), i32(inp.positions, dev), cache, qk_norm=qk,
+                      status=status)
+    torch.cuda.synchronize()
+    return q, k_pool, v_pool, int(status.item())
+
+
+@pytest.mark.parametrize("norm", [False, True], ids=["rope", "rope_qknorm"])
+@pytest.mark.parametrize("base", [1e4, 1e6])
+def test_kv_store_rope_parity(norm, base):
+    T, hq, hkv = 300, 32, 8
+    log(f"kv_store_rope T={T} Hq={hq} Hkv={hkv} base={base} norm={norm}")
+    inp = rope_inputs(17, T, hq, hkv)
+    q, k_pool, v_pool, st = run_rope(inp, hq, hkv, base, norm)
+    assert st == 0
+    q_ref, rows = R.store_kv_rope(inp.q, inp.k, inp.v, inp.out_loc, inp.positions, base,
+                                  (inp.q_weight, inp.k_weight, NORM_EPS) if norm else None)
+    assert_rows_close(bits(q), q_ref, "q")
+    locs = np.array(sorted(rows), dtype=np.int64)
+    kb = bits(k_pool[torch.from_numpy(locs).cuda()])
+    vb = bits(v_pool[torch.from_numpy(locs).cuda()])
+    assert_rows_close(kb, np.stack([rows[int(r)][0] for r in locs]), "k rows")
+    assert np.array_equal(vb, np.stack([rows[int(r)][1] for r in locs])), "v rows"
+    # rows nobody wrote stay zero
+    untouched = np.setdiff1d(np.arange(inp.num_pool_rows), locs)[:512]
+    assert not bits(k_pool[torch.from_numpy(untouched).cuda()]).any()
+
+
+def test_kv_store_rope_strided_pool_and_group16():
+    """A layer-interleaved pool (row stride 3x the row) and 16 query heads per KV head."""
+    T, hq, hkv = 64, 32, 2
+    inp = rope_inputs(23, T, hq, hkv, max_position=4096)
+    q, k_pool, v_pool, st = run_rope(inp, hq, hkv, 1e4, True, row_stride=3 * hkv * D)
+    assert st == 0
+    q_ref, rows = R.store_kv_rope(inp.q, inp.k, inp.v, inp.out_loc, inp.positions, 1e4,
+                                  (inp.q_weight, inp.k_weight, NORM_EPS))
+    assert_rows_close(bits(q), q_ref, "q")
+    locs = np.array(sorted(rows), dtype=np.int64)
+    assert_rows_close(bits(k_pool[torch.from_numpy(locs).cuda()]), np.stack([rows[int(r)][0] for r in locs]), "k")
+    assert np.array_equal(bits(v_pool[torch.from_numpy(locs).cuda()]), np.stack([rows[int(r)][1] for r in locs]))
+
+
+def test_kv_store_rope_bad_position_and_row():
+    T, hq, hkv = 8, 8, 8
+    inp = rope_inputs(29, T, hq, hkv, max_position=1024)
+    inp.positions[2] = 1024          # past the table: token untouched
+    inp.positions[3] = -1
+    inp.out_loc[5] = inp.num_pool_rows  # outside the pool: q rotated, nothing stored
+    q, k_pool, v_pool, st = run_rope(inp, hq, hkv, 1e4, False)
+    assert st == (pkv.PKV_STATUS_BAD_POSITION | pkv.PKV_STATUS_BAD_OUT_LOC)
+    qb = bits(q)
+    assert np.array_equal(qb[2], inp.q[2]) and np.array_equal(qb[3], inp.q[3])
+    q_ref, rows = R.store_kv_rope(inp.q[[5]], inp.k[[5]], inp.v[[5]], np.array([1]), inp.positions[[5]], 1e4)
+    assert_rows_close(qb[[5]], q_ref, "q of the token with a bad row")
+    for t in (0, 1, 4, 6, 7):
+        r = int(inp.out_loc[t])
+        assert np.array_equal(bits(v_pool[r]), inp.v[t])
+    for t in (2, 3):
+        assert not bits(v_pool[int(inp.out_loc[t])]).any()
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_kv_store_rope_full_size_sampled(cfg):
+    """The token counts and head shapes of the serving-decode (256 tokens) and
+    shared-prefix extend (8192 tokens) batches, 2^20-row pool, positions up to
+    32K; sampled tokens checked one by one."""
+    T = {2: 256, 3: 8192}[cfg]
+    hq, hkv = 32, 8
+    inp = rope_inputs(100 + cfg, T, hq, hkv, num_pool_rows=1 << 20)
+    log(f"kv_store_rope full size T={T}")
+    q, k_pool, v_pool, st = run_rope(inp, hq, hkv, 1e6, True)
+    assert st == 0
+    idx = np.unique(np.r_[0, T - 1, np.random.default_rng(cfg).integers(0, T, 64)])
+    q_ref, rows = R.store_kv_rope(inp.q[idx], inp.k[idx], inp.v[idx], inp.out_loc[idx], inp.positions[idx], 1e6,
+                                  (inp.q_weight, inp.k_weight, NORM_EPS))
+    assert_rows_close(bits(q)[idx], q_ref, "q")
+    locs = inp.out_loc[idx].astype(np.int64)
+    assert_rows_close(bits(k_pool[torch.from_numpy(locs).cuda()]), np.stack([rows[int(r)][0] for r in locs]), "k")
+    assert np.array_equal(bits(v_pool[torch.from_numpy(locs).cuda()]), np.stack([rows[int(r)][1] for r in locs]))
