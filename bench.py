@@ -100,6 +100,45 @@ def cpu_baseline(w, kind: str, budget_s: float):
             "seconds": round(elapsed, 2)}
 
 
+def rope_measurement(ds, w, args, stream, PM):
+    """kv_store_rope (RoPE with Qwen3-style per-head q/k RMS norm, base 1e6) on
+    the step's tokens at their metadata positions and rows; timed on its own,
+    after the step (it rotates q in place)."""
+    import torch
+    import paged_kv_attention_08_amd as pkv
+    from workloads.rope_inputs import NORM_EPS, rope_inputs
+
+    T = w.num_tokens
+    max_pos = int(w.device_len.max()) + 1
+    cache = torch.empty((max_pos, w.head_dim), dtype=torch.float32, device="cuda")
+    pkv.rope_cos_sin_cache(cache, 1e6)
+    inp = rope_inputs(7, 1, w.num_qo_heads, w.num_kv_heads, w.head_dim)  # only the norm weights are used
+    from tests.gpu_harness import bf16_tensor
+    norm = (bf16_tensor(inp.q_weight, "cuda"), bf16_tensor(inp.k_weight, "cuda"), NORM_EPS)
+    out_loc, positions = ds.meta.out_loc[:T], ds.meta.positions[:T]
+
+    def launch():
+        pkv.kv_store_rope(ds.pool, ds.q, ds.k_new, ds.v_new, out_loc, positions, cache, qk_norm=norm,
+                          status=ds.meta.status, stream=stream)
+
+    for _ in range(args.warmup):
+        launch()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        launch()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    assert ds.status() == 0, f"device status {ds.status():#x}"
+    ms = ev[0].elapsed_time(ev[1]) / args.steps
+    nbytes = PM.rope_store_bytes(T, w.num_qo_heads, w.num_kv_heads, w.head_dim)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"tokens": T, "avg_launch_ms": round(ms, 4), "algorithmic_bytes_per_launch": nbytes,
+            "achieved_gbps": round(gbps, 1), "roofline": {"bound": "hbm", "peak": PM.HBM_PEAK_GBPS,
+                                                          "frac": round(gbps / PM.HBM_PEAK_GBPS, 4)},
+            "what": "RoPE base 1e6 + per-head q/k RMS norm fused into the K/V store"}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,6 +282,7 @@ def main(argv=None):
         "store_gbps": round(store_gbps, 1),
         "roofline": roof,
     }
+    out["next_rows"] = {"kv_store_rope": rope_measurement(ds, w, args, stream, PM)}
     ds.free()
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")

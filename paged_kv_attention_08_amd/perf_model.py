@@ -44,3 +44,14 @@ def extend_flops(cached_len, device_len, num_qo_heads: int, head_dim: int) -> in
     n = np.asarray(device_len, dtype=np.int64) - c
     pairs = (n * c + n * (n + 1) // 2).sum()
     return int(4 * num_qo_heads * head_dim * pairs)
+
+
+def rope_store_bytes(num_tokens: int, num_qo_heads: int, num_kv_heads: int, head_dim: int,
+                     qk_norm: bool = True) -> int:
+    """kv_store_rope: q read and written, k and v read, two pool rows written,
+    out_loc and positions read, one float table row (head_dim floats) per
+    token, the two norm weight rows once."""
+    t = int(num_tokens)
+    q = 2 * t * num_qo_heads * head_dim * 2
+    kv = 2 * t * num_kv_heads * head_dim * 2
+    return q + 2 * kv + 8 * t + t * head_dim * 4 + (2 * head_dim * 2 if qk_norm else 0)
