@@ -100,6 +100,44 @@ def cpu_baseline(w, kind: str, budget_s: float):
             "seconds": round(elapsed, 2)}
 
 
+def graph_measurement(ds, w, args, stream):
+    """The decode step (metadata, store, decode attention) replayed as one HIP
+    graph captured for this batch size, against the same three calls issued
+    eagerly; per-step latency from events around K back-to-back steps."""
+    import torch
+    import paged_kv_attention_08_amd as pkv
+
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    graph = pkv.DecodeGraph(ds.pool, ds.page_table, ds.batch, ds.alloc_rows, ds.q, ds.o, ds.k_new, ds.v_new,
+                            ds.meta, ds.workspace, w.sm_scale, int(w.dummy_table_row), [w.num_reqs], side)
+    try:
+        def timed(fn):
+            for _ in range(args.warmup):
+                fn()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            side.synchronize()
+            ev[0].record(side)
+            for _ in range(args.steps):
+                fn()
+            ev[1].record(side)
+            torch.cuda.synchronize()
+            return ev[0].elapsed_time(ev[1]) / args.steps
+
+        def eager():
+            ds.metadata(side)
+            ds.store(side)
+            ds.decode(side)
+
+        eager_ms = timed(eager)
+        graph_ms = timed(lambda: graph.replay(w.num_reqs, stream=side))
+    finally:
+        graph.close()
+    assert ds.status() == 0, f"device status {ds.status():#x}"
+    return {"batch": w.num_reqs, "eager_step_ms": round(eager_ms, 4), "graph_step_ms": round(graph_ms, 4),
+            "what": "build_attn_metadata + kv_store + paged_decode_attn, eager launches vs one graph replay"}
+
+
 def rope_measurement(ds, w, args, stream, PM):
     """kv_store_rope (RoPE with Qwen3-style per-head q/k RMS norm, base 1e6) on
     the step's tokens at their metadata positions and rows; timed on its own,
@@ -282,7 +320,10 @@ def main(argv=None):
         "store_gbps": round(store_gbps, 1),
         "roofline": roof,
     }
-    out["next_rows"] = {"kv_store_rope": rope_measurement(ds, w, args, stream, PM)}
+    out["next_rows"] = {}
+    if has_decode and not has_extend:
+        out["next_rows"]["decode_graph"] = graph_measurement(ds, w, args, stream)
+    out["next_rows"]["kv_store_rope"] = rope_measurement(ds, w, args, stream, PM)
     ds.free()
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")

@@ -252,6 +252,61 @@ int kv_store_rope(const pkv_kv_pool* pool, void* q, int32_t num_qo_heads, const 
                   const float* cos_sin_cache, int32_t max_position, const pkv_qk_norm* qk_norm,
                   int32_t* status, void* stream);
 
+/* ---- decode step as HIP graphs ------------------------------------------ */
+
+/* The fixed buffers of a graph-replayed decode step (deep dive 4.3, learning
+ * notes graph passage: every input, output and workspace keeps the address it
+ * had at capture).  All device pointers, sized for max_reqs requests (one
+ * token each): */
+typedef struct pkv_decode_graph_desc {
+  pkv_kv_pool pool;
+  pkv_page_table page_table;
+  int32_t max_reqs;
+  int32_t dummy_table_row;     /* an all-zero page-table row: padding requests use it */
+  int32_t num_qo_heads;
+  float sm_scale;
+  int32_t* table_idx;          /* int32 [max_reqs] */
+  int32_t* cached_len;         /* int32 [max_reqs] */
+  int32_t* device_len;         /* int32 [max_reqs] */
+  int32_t* alloc_rows;         /* int32 [max_reqs]: new-page rows, as for build_attn_metadata */
+  const void* q;               /* bf16 [max_reqs, Hq, head_dim] */
+  void* o;                     /* bf16 [max_reqs, Hq, head_dim] */
+  const void* k_new;           /* bf16 [max_reqs, Hkv, head_dim] */
+  const void* v_new;           /* bf16 [max_reqs, Hkv, head_dim] */
+  pkv_attn_metadata meta;      /* buffers for (max_reqs requests, max_reqs tokens) */
+  void* workspace;             /* >= paged_attn_workspace_bytes(max_reqs, Hq, head_dim) */
+  size_t workspace_bytes;
+  int32_t reserved;            /* must be 0 */
+} pkv_decode_graph_desc;
+
+typedef struct pkv_decode_graph pkv_decode_graph;  /* opaque, host side */
+
+/* pkv_decode_graph_create: capture, for each batch size in sizes (host array,
+ * strictly increasing, each <= max_reqs; the pages' list is 1, 2, 4, 8, 16, ...),
+ * one graph of build_attn_metadata -> kv_store (at the metadata's out_loc) ->
+ * paged_decode_attn on a decode batch of that many requests in desc's
+ * buffers.  stream must be a non-default stream (capture happens on it; the
+ * buffers' contents are not read during capture).  This is the one call that
+ * allocates: host memory and the graphs' driver objects, no device memory,
+ * released by pkv_decode_graph_destroy.  A failing host check of any of the
+ * three calls is returned and nothing is kept. */
+int pkv_decode_graph_create(const pkv_decode_graph_desc* desc, const int32_t* sizes, int32_t num_sizes,
+                            pkv_decode_graph** graph, void* stream);
+
+/* pkv_decode_graph_replay: the caller has written its num_reqs real decode
+ * requests into slots [0, num_reqs) of table_idx / cached_len / device_len /
+ * q / k_new / v_new and their num_alloc new-page rows into alloc_rows[0,
+ * num_alloc) (num_alloc <= num_reqs; with page_size 1 it equals num_reqs).
+ * The call picks the smallest captured size bs >= num_reqs (written to
+ * *graph_size if non-NULL), turns slots [num_reqs, bs) into dummy requests on
+ * dummy_table_row (cached_len 0, device_len 1, new row 0 on the dummy page),
+ * and launches that graph on stream.  Outputs of the real requests are in
+ * o[0, num_reqs).  Replays on one graph object must not overlap. */
+int pkv_decode_graph_replay(pkv_decode_graph* graph, int32_t num_reqs, int32_t num_alloc, int32_t* graph_size,
+                            void* stream);
+
+int pkv_decode_graph_destroy(pkv_decode_graph* graph);
+
 /* ---- diagnostics -------------------------------------------------------- */
 const char* pkv_error_string(int code);   /* static string, never NULL */
 int         pkv_last_hip_error(void);      /* hipError_t of the last PKV_ERR_HIP in this thread */

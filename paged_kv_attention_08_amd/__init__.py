@@ -24,7 +24,7 @@ from ._lib import (PKV_STATUS_BAD_ALLOC, PKV_STATUS_BAD_DECODE, PKV_STATUS_BAD_L
 
 __all__ = ["PagedKVError", "KVPoolTensors", "BatchTensors", "MetadataBuffers", "kv_store", "build_attn_metadata",
            "paged_decode_attn", "paged_extend_attn", "plan_bytes", "workspace_bytes", "library_path",
-           "rope_cos_sin_cache", "kv_store_rope", "PKV_STATUS_BAD_POSITION",
+           "rope_cos_sin_cache", "kv_store_rope", "PKV_STATUS_BAD_POSITION", "DecodeGraph",
            "PKV_STATUS_BAD_ALLOC", "PKV_STATUS_BAD_DECODE", "PKV_STATUS_BAD_LENGTHS", "PKV_STATUS_BAD_OUT_LOC",
            "PKV_STATUS_BAD_PAGE_ROW", "PKV_STATUS_BAD_TABLE_IDX", "PKV_STATUS_TOKEN_COUNT"]
 
@@ -259,3 +259,69 @@ def kv_store_rope(pool: KVPoolTensors, q: torch.Tensor, k_new: torch.Tensor, v_n
         ctypes.byref(p), q.data_ptr(), q.shape[1], k_new.data_ptr(), v_new.data_ptr(), out_loc.data_ptr(),
         positions.data_ptr(), t, cos_sin_cache.data_ptr(), cos_sin_cache.shape[0],
         ctypes.byref(norm) if norm is not None else None, _ptr(status), _stream(stream)))
+
+
+class DecodeGraph:
+    """The decode step (build_attn_metadata -> kv_store -> paged_decode_attn)
+    captured as one HIP graph per batch size in `sizes` over fixed buffers
+    sized for max_reqs requests; replay(n) pads to the smallest captured size
+    >= n with dummy requests on `dummy_table_row` and launches that graph."""
+
+    def __init__(self, pool: KVPoolTensors, page_table: torch.Tensor, batch: BatchTensors, alloc_rows: torch.Tensor,
+                 q: torch.Tensor, o: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, meta: MetadataBuffers,
+                 workspace: torch.Tensor, sm_scale: float, dummy_table_row: int, sizes, stream):
+        if stream is None or _stream(stream) == 0:
+            raise ValueError("graph capture needs a non-default stream")
+        _need(page_table, "page_table", torch.int32, 2)
+        _need(alloc_rows, "alloc_rows", torch.int32, 1)
+        for name, x in (("q", q), ("o", o), ("k_new", k_new), ("v_new", v_new)):
+            _need(x, name, torch.bfloat16, 3)
+        max_reqs = batch.table_idx.numel()
+        if (q.shape[0] < max_reqs or o.shape != q.shape or k_new.shape[0] < max_reqs or v_new.shape != k_new.shape
+                or alloc_rows.numel() < max_reqs or batch.cached_len.numel() < max_reqs
+                or batch.device_len.numel() < max_reqs):
+            raise ValueError("graph buffers must hold max_reqs requests")
+        _need(workspace, "workspace", workspace.dtype, 1)
+        self._keep = (pool, page_table, batch, alloc_rows, q, o, k_new, v_new, meta, workspace)
+        d = _lib.DecodeGraphDesc()
+        d.pool = pool.struct()
+        d.page_table = _lib.PageTable(page_table.data_ptr(), page_table.shape[0], page_table.shape[1])
+        d.max_reqs = max_reqs
+        d.dummy_table_row = dummy_table_row
+        d.num_qo_heads = q.shape[1]
+        d.sm_scale = float(sm_scale)
+        d.table_idx, d.cached_len = batch.table_idx.data_ptr(), batch.cached_len.data_ptr()
+        d.device_len, d.alloc_rows = batch.device_len.data_ptr(), alloc_rows.data_ptr()
+        d.q, d.o, d.k_new, d.v_new = q.data_ptr(), o.data_ptr(), k_new.data_ptr(), v_new.data_ptr()
+        d.meta = meta.struct()
+        d.workspace = workspace.data_ptr()
+        d.workspace_bytes = workspace.numel() * workspace.element_size()
+        d.reserved = 0
+        self.sizes = sorted(int(x) for x in sizes)
+        arr = (ctypes.c_int32 * len(self.sizes))(*self.sizes)
+        handle = ctypes.c_void_p()
+        self._stream = stream
+        _check("pkv_decode_graph_create",
+               _lib.lib().pkv_decode_graph_create(ctypes.byref(d), arr, len(self.sizes), ctypes.byref(handle),
+                                                  _stream(stream)))
+        self._handle = handle
+
+    def replay(self, num_reqs: int, num_alloc: Optional[int] = None, stream=None) -> int:
+        """Launch the graph for num_reqs real requests already written to the
+        buffers' first slots; returns the padded batch size used."""
+        bs = ctypes.c_int32(0)
+        _check("pkv_decode_graph_replay",
+               _lib.lib().pkv_decode_graph_replay(self._handle, num_reqs, num_reqs if num_alloc is None else num_alloc,
+                                                  ctypes.byref(bs), _stream(stream or self._stream)))
+        return bs.value
+
+    def close(self) -> None:
+        if getattr(self, "_handle", None) is not None and self._handle.value:
+            _lib.lib().pkv_decode_graph_destroy(self._handle)
+            self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001 - interpreter shutdown
+            pass

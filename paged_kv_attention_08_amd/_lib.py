@@ -49,6 +49,14 @@ class QKNorm(ctypes.Structure):
     _fields_ = [("q_weight", c_void_p), ("k_weight", c_void_p), ("eps", c_float), ("reserved", c_int32)]
 
 
+class DecodeGraphDesc(ctypes.Structure):
+    _fields_ = [("pool", KVPool), ("page_table", PageTable), ("max_reqs", c_int32), ("dummy_table_row", c_int32),
+                ("num_qo_heads", c_int32), ("sm_scale", c_float), ("table_idx", c_void_p), ("cached_len", c_void_p),
+                ("device_len", c_void_p), ("alloc_rows", c_void_p), ("q", c_void_p), ("o", c_void_p),
+                ("k_new", c_void_p), ("v_new", c_void_p), ("meta", AttnMetadata), ("workspace", c_void_p),
+                ("workspace_bytes", c_size_t), ("reserved", c_int32)]
+
+
 # name -> (restype, argtypes); the exports of include/pagedkv.h
 PROTOTYPES = {
     "pkv_plan_bytes": (c_size_t, [c_int32, c_int64, c_int32, c_int32]),
@@ -63,6 +71,10 @@ PROTOTYPES = {
     "pkv_rope_cos_sin_cache": (c_int, [c_void_p, c_int32, c_int32, ctypes.c_double, c_void_p]),
     "kv_store_rope": (c_int, [POINTER(KVPool), c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int64,
                               c_void_p, c_int32, POINTER(QKNorm), c_void_p, c_void_p]),
+    "pkv_decode_graph_create": (c_int, [POINTER(DecodeGraphDesc), POINTER(c_int32), c_int32, POINTER(c_void_p),
+                                        c_void_p]),
+    "pkv_decode_graph_replay": (c_int, [c_void_p, c_int32, c_int32, POINTER(c_int32), c_void_p]),
+    "pkv_decode_graph_destroy": (c_int, [c_void_p]),
     "pkv_error_string": (ctypes.c_char_p, [c_int]),
     "pkv_last_hip_error": (c_int, []),
     "pkv_version": (c_int, []),

@@ -6,7 +6,7 @@
 
 using namespace pkv;
 
-namespace {
+namespace pkv {
 
 thread_local int g_last_hip_error = 0;
 
@@ -14,6 +14,11 @@ int hip_failed(hipError_t e) {
   g_last_hip_error = (int)e;
   return PKV_ERR_HIP;
 }
+
+}  // namespace pkv
+
+namespace {
+
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

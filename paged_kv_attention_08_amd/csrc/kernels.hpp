@@ -85,6 +85,9 @@ struct AttnArgs {
   int32_t* status;
 };
 
+// records e as the thread's last HIP error and returns PKV_ERR_HIP
+int hip_failed(hipError_t e);
+
 hipError_t launch_kv_store(const StoreArgs& a, hipStream_t s);
 hipError_t launch_kv_store_rope(const RopeArgs& a, hipStream_t s);
 hipError_t launch_rope_cache(const RopeCacheArgs& a, hipStream_t s);

@@ -216,3 +216,28 @@ def test_kv_store_rope_rejects(lib, kw, code):
 ])
 def test_rope_cache_rejects(lib, args, code):
     assert lib.pkv_rope_cos_sin_cache(*args, None) == code
+
+
+def test_decode_graph_rejects_before_capture(lib):
+    d = _lib.DecodeGraphDesc()
+    sizes = (ctypes.c_int32 * 3)(1, 2, 4)
+    h = ctypes.c_void_p()
+    assert lib.pkv_decode_graph_create(None, sizes, 3, ctypes.byref(h), FAKE) == _lib.PKV_ERR_INVALID_ARGUMENT
+    assert lib.pkv_decode_graph_create(ctypes.byref(d), sizes, 3, ctypes.byref(h), FAKE) == \
+        _lib.PKV_ERR_INVALID_ARGUMENT                     # max_reqs 0, null buffers
+    d.max_reqs = 4
+    for name in ("table_idx", "cached_len", "device_len", "alloc_rows", "q", "o", "k_new", "v_new"):
+        setattr(d, name, FAKE)
+    d.page_table = _lib.PageTable(FAKE, 8, 32)
+    d.dummy_table_row = 8                                 # outside the table
+    assert lib.pkv_decode_graph_create(ctypes.byref(d), sizes, 3, ctypes.byref(h), FAKE) == \
+        _lib.PKV_ERR_INVALID_ARGUMENT
+    d.dummy_table_row = 7
+    bad = (ctypes.c_int32 * 3)(1, 4, 2)                   # not increasing
+    assert lib.pkv_decode_graph_create(ctypes.byref(d), bad, 3, ctypes.byref(h), FAKE) == _lib.PKV_ERR_INVALID_ARGUMENT
+    big = (ctypes.c_int32 * 3)(1, 2, 8)                   # beyond max_reqs
+    assert lib.pkv_decode_graph_create(ctypes.byref(d), big, 3, ctypes.byref(h), FAKE) == _lib.PKV_ERR_INVALID_ARGUMENT
+    assert lib.pkv_decode_graph_create(ctypes.byref(d), sizes, 3, ctypes.byref(h), None) == \
+        _lib.PKV_ERR_INVALID_ARGUMENT                     # the default stream cannot be captured
+    assert lib.pkv_decode_graph_replay(None, 1, 1, None, FAKE) == _lib.PKV_ERR_INVALID_ARGUMENT
+    assert lib.pkv_decode_graph_destroy(None) == _lib.PKV_ERR_INVALID_ARGUMENT
