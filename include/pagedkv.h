@@ -64,6 +64,8 @@ extern "C" {
 #define PKV_STATUS_TOKEN_COUNT    0x20  /* sum of extend_len differs from num_tokens */
 #define PKV_STATUS_BAD_ALLOC      0x40  /* alloc_rows entry misaligned, outside the pool, or too few entries */
 #define PKV_STATUS_BAD_POSITION   0x80  /* positions[t] outside [0, max_position): token skipped by kv_store_rope */
+#define PKV_STATUS_OUT_OF_PAGES   0x100 /* the free list held fewer pages than the batch needs: nothing allocated */
+#define PKV_STATUS_FREE_OVERFLOW  0x200 /* freeing would overfill the free list: nothing freed */
 
 /* ---- data structures ---------------------------------------------------- */
 
@@ -169,7 +171,10 @@ int kv_store(const pkv_kv_pool* pool, const void* k_new, const void* v_new, cons
  *   num_qo_heads, num_kv_heads : head counts the plan is built for; the
  *                attention calls must use the same ones.
  * Requests with invalid lengths or table_idx are skipped (status bit set);
- * entries outside [cached_len, device_len) of each row are left untouched. */
+ * entries outside [cached_len, device_len) of each row are left untouched.
+ * A token that gets no row (its request skipped, a bad alloc or page-table
+ * entry, or past the batch's real tokens) has out_loc and positions set to
+ * -1, which kv_store and kv_store_rope skip. */
 int build_attn_metadata(const pkv_batch* batch, const pkv_page_table* page_table, int32_t page_size,
                         int64_t num_pool_rows, const int32_t* alloc_rows, int64_t num_alloc,
                         int32_t num_qo_heads, int32_t num_kv_heads, const pkv_attn_metadata* meta,
@@ -251,6 +256,45 @@ int kv_store_rope(const pkv_kv_pool* pool, void* q, int32_t num_qo_heads, const 
                   const int32_t* out_loc, const int32_t* positions, int64_t num_tokens,
                   const float* cos_sin_cache, int32_t max_position, const pkv_qk_norm* qk_norm,
                   int32_t* status, void* stream);
+
+/* ---- page allocator on the GPU ------------------------------------------- */
+
+/* A free list of page-start rows kept on the device as a ring (learning
+ * notes, page-table passage: free_slots, page aligned; deep dive 3.6: freed
+ * entries are appended).  The oldest free page is rows[state[0]]; state[1]
+ * pages are free, at ring positions state[0], state[0] + 1, ... (mod
+ * capacity).  Concurrent calls on one free list race. */
+typedef struct pkv_free_list {
+  int32_t* rows;           /* int32 [capacity], device */
+  int32_t* state;          /* int32 [2], device: head, number of free pages */
+  int32_t capacity;        /* > 0 */
+  int32_t page_size;       /* a power of two <= 64; every row is a multiple of it */
+  int64_t num_pool_rows;   /* rows of the pool the pages belong to */
+} pkv_free_list;
+
+/* pkv_free_list_reset: the caller has written num_free page-start rows to
+ * rows[0, num_free); sets head 0 and num_free free pages (0 <= num_free <= capacity). */
+int pkv_free_list_reset(const pkv_free_list* free_list, int32_t num_free, void* stream);
+
+/* pkv_alloc_pages: request i of the batch needs
+ *   ceil(device_len/s) - ceil(cached_len/s) pages (0 unless 0 <= cached_len <= device_len),
+ * the page-aligned count over [cached_len, device_len); the batch takes the
+ * next n = sum of them oldest-first, request by request, into alloc_rows[0, n)
+ * (the alloc_rows input of build_attn_metadata for the same batch), and the
+ * list loses them.  If fewer than n are free, or n > max_alloc, nothing is
+ * taken, alloc_rows[0, min(n, max_alloc)) are set to -1 (build_attn_metadata
+ * then maps none of the batch's new tokens) and PKV_STATUS_OUT_OF_PAGES is
+ * raised: the caller evicts and retries.  A row that is not page aligned or
+ * outside the pool is passed on and raises PKV_STATUS_BAD_ALLOC. */
+int pkv_alloc_pages(const pkv_free_list* free_list, const pkv_batch* batch, int32_t* alloc_rows, int64_t max_alloc,
+                    int32_t* status, void* stream);
+
+/* pkv_free_pages: appends rows[0, num_rows) (device, page-start rows) to the
+ * free list in order.  Nothing is freed if one of them is not a page-aligned
+ * row of the pool (PKV_STATUS_BAD_ALLOC) or the list would exceed its
+ * capacity (PKV_STATUS_FREE_OVERFLOW). */
+int pkv_free_pages(const pkv_free_list* free_list, const int32_t* rows, int32_t num_rows, int32_t* status,
+                   void* stream);
 
 /* ---- decode step as HIP graphs ------------------------------------------ */
 

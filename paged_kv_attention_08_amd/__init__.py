@@ -20,11 +20,12 @@ import torch
 from . import _lib
 from ._lib import (PKV_STATUS_BAD_ALLOC, PKV_STATUS_BAD_DECODE, PKV_STATUS_BAD_LENGTHS, PKV_STATUS_BAD_OUT_LOC,
                    PKV_STATUS_BAD_PAGE_ROW, PKV_STATUS_BAD_POSITION, PKV_STATUS_BAD_TABLE_IDX,
-                   PKV_STATUS_TOKEN_COUNT)
+                   PKV_STATUS_FREE_OVERFLOW, PKV_STATUS_OUT_OF_PAGES, PKV_STATUS_TOKEN_COUNT)
 
 __all__ = ["PagedKVError", "KVPoolTensors", "BatchTensors", "MetadataBuffers", "kv_store", "build_attn_metadata",
            "paged_decode_attn", "paged_extend_attn", "plan_bytes", "workspace_bytes", "library_path",
-           "rope_cos_sin_cache", "kv_store_rope", "PKV_STATUS_BAD_POSITION", "DecodeGraph",
+           "rope_cos_sin_cache", "kv_store_rope", "PKV_STATUS_BAD_POSITION", "DecodeGraph", "PageFreeList",
+           "PKV_STATUS_OUT_OF_PAGES", "PKV_STATUS_FREE_OVERFLOW",
            "PKV_STATUS_BAD_ALLOC", "PKV_STATUS_BAD_DECODE", "PKV_STATUS_BAD_LENGTHS", "PKV_STATUS_BAD_OUT_LOC",
            "PKV_STATUS_BAD_PAGE_ROW", "PKV_STATUS_BAD_TABLE_IDX", "PKV_STATUS_TOKEN_COUNT"]
 
@@ -325,3 +326,52 @@ class DecodeGraph:
             self.close()
         except Exception:  # noqa: BLE001 - interpreter shutdown
             pass
+
+
+class PageFreeList:
+    """A device-resident ring of free page-start rows (oldest first) that
+    pkv_alloc_pages takes a batch's new pages from and pkv_free_pages appends
+    to; its state (head, count) stays on the device."""
+
+    def __init__(self, capacity: int, page_size: int, num_pool_rows: int, device="cuda"):
+        self.rows = torch.zeros(capacity, dtype=torch.int32, device=device)
+        self.state = torch.zeros(2, dtype=torch.int32, device=device)
+        self.capacity, self.page_size, self.num_pool_rows = int(capacity), int(page_size), int(num_pool_rows)
+
+    def struct(self) -> _lib.FreeList:
+        return _lib.FreeList(self.rows.data_ptr(), self.state.data_ptr(), self.capacity, self.page_size,
+                             self.num_pool_rows)
+
+    def reset(self, free_rows: torch.Tensor, stream=None) -> None:
+        """Start from free_rows (int32 page-start rows, oldest first)."""
+        _need(free_rows, "free_rows", torch.int32, 1)
+        n = free_rows.numel()
+        if n > self.capacity:
+            raise ValueError("more free rows than capacity")
+        self.rows[:n].copy_(free_rows)
+        f = self.struct()
+        _check("pkv_free_list_reset", _lib.lib().pkv_free_list_reset(ctypes.byref(f), n, _stream(stream)))
+
+    def alloc(self, batch: BatchTensors, alloc_rows: torch.Tensor, status: Optional[torch.Tensor] = None,
+              stream=None) -> None:
+        """The batch's new pages into alloc_rows (oldest free pages first, request by request)."""
+        f, b = self.struct(), batch.struct()
+        _need(alloc_rows, "alloc_rows", torch.int32, 1)
+        if status is not None:
+            _need(status, "status", torch.int32, 1)
+        _check("pkv_alloc_pages", _lib.lib().pkv_alloc_pages(ctypes.byref(f), ctypes.byref(b), alloc_rows.data_ptr(),
+                                                             alloc_rows.numel(), _ptr(status), _stream(stream)))
+
+    def free(self, rows: torch.Tensor, status: Optional[torch.Tensor] = None, stream=None) -> None:
+        f = self.struct()
+        _need(rows, "rows", torch.int32, 1)
+        if status is not None:
+            _need(status, "status", torch.int32, 1)
+        _check("pkv_free_pages", _lib.lib().pkv_free_pages(ctypes.byref(f), rows.data_ptr() if rows.numel() else None,
+                                                           rows.numel(), _ptr(status), _stream(stream)))
+
+    def snapshot(self):
+        """The free rows, oldest first (host copy; synchronises)."""
+        head, count = (int(x) for x in self.state.cpu())
+        rows = self.rows.cpu().numpy()
+        return [int(rows[(head + k) % self.capacity]) for k in range(count)]

@@ -23,6 +23,8 @@ PKV_STATUS_BAD_DECODE = 0x10
 PKV_STATUS_TOKEN_COUNT = 0x20
 PKV_STATUS_BAD_ALLOC = 0x40
 PKV_STATUS_BAD_POSITION = 0x80
+PKV_STATUS_OUT_OF_PAGES = 0x100
+PKV_STATUS_FREE_OVERFLOW = 0x200
 
 
 class KVPool(ctypes.Structure):
@@ -49,6 +51,11 @@ class QKNorm(ctypes.Structure):
     _fields_ = [("q_weight", c_void_p), ("k_weight", c_void_p), ("eps", c_float), ("reserved", c_int32)]
 
 
+class FreeList(ctypes.Structure):
+    _fields_ = [("rows", c_void_p), ("state", c_void_p), ("capacity", c_int32), ("page_size", c_int32),
+                ("num_pool_rows", c_int64)]
+
+
 class DecodeGraphDesc(ctypes.Structure):
     _fields_ = [("pool", KVPool), ("page_table", PageTable), ("max_reqs", c_int32), ("dummy_table_row", c_int32),
                 ("num_qo_heads", c_int32), ("sm_scale", c_float), ("table_idx", c_void_p), ("cached_len", c_void_p),
@@ -71,6 +78,9 @@ PROTOTYPES = {
     "pkv_rope_cos_sin_cache": (c_int, [c_void_p, c_int32, c_int32, ctypes.c_double, c_void_p]),
     "kv_store_rope": (c_int, [POINTER(KVPool), c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int64,
                               c_void_p, c_int32, POINTER(QKNorm), c_void_p, c_void_p]),
+    "pkv_free_list_reset": (c_int, [POINTER(FreeList), c_int32, c_void_p]),
+    "pkv_alloc_pages": (c_int, [POINTER(FreeList), POINTER(Batch), c_void_p, c_int64, c_void_p, c_void_p]),
+    "pkv_free_pages": (c_int, [POINTER(FreeList), c_void_p, c_int32, c_void_p, c_void_p]),
     "pkv_decode_graph_create": (c_int, [POINTER(DecodeGraphDesc), POINTER(c_int32), c_int32, POINTER(c_void_p),
                                         c_void_p]),
     "pkv_decode_graph_replay": (c_int, [c_void_p, c_int32, c_int32, POINTER(c_int32), c_void_p]),

@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
-SOURCES = ["api.hip", "kv_store.hip", "rope.hip", "graph.hip", "metadata.hip", "decode.hip", "extend.hip"]
+SOURCES = ["api.hip", "kv_store.hip", "rope.hip", "graph.hip", "alloc.hip", "metadata.hip", "decode.hip", "extend.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -224,6 +224,67 @@ int paged_extend_attn(const pkv_kv_pool* pool, const pkv_page_table* page_table,
   return e == hipSuccess ? PKV_OK : hip_failed(e);
 }
 
+namespace {
+
+int check_free_list(const pkv_free_list* f) {
+  if (!f || !f->rows || !f->state || f->capacity <= 0) return PKV_ERR_INVALID_ARGUMENT;
+  if (!pow2_le64(f->page_size)) return PKV_ERR_UNSUPPORTED;
+  if (f->num_pool_rows <= 0 || f->num_pool_rows >= (int64_t(1) << 31) || f->num_pool_rows % f->page_size != 0)
+    return PKV_ERR_INVALID_ARGUMENT;
+  return PKV_OK;
+}
+
+AllocArgs alloc_args(const pkv_free_list* f, int32_t* status) {
+  AllocArgs a{};
+  a.rows = f->rows;
+  a.state = f->state;
+  a.capacity = f->capacity;
+  a.page_size = f->page_size;
+  a.num_pool_rows = f->num_pool_rows;
+  a.status = status;
+  return a;
+}
+
+}  // namespace
+
+int pkv_free_list_reset(const pkv_free_list* free_list, int32_t num_free, void* stream) {
+  int rc = check_free_list(free_list);
+  if (rc != PKV_OK) return rc;
+  if (num_free < 0 || num_free > free_list->capacity) return PKV_ERR_INVALID_ARGUMENT;
+  hipError_t e = launch_free_list_reset(free_list->state, num_free, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : hip_failed(e);
+}
+
+int pkv_alloc_pages(const pkv_free_list* free_list, const pkv_batch* batch, int32_t* alloc_rows, int64_t max_alloc,
+                    int32_t* status, void* stream) {
+  int rc = check_free_list(free_list);
+  if (rc != PKV_OK) return rc;
+  if ((rc = check_batch(batch)) != PKV_OK) return rc;
+  if (max_alloc < 0 || (max_alloc > 0 && !alloc_rows)) return PKV_ERR_INVALID_ARGUMENT;
+  if (batch->num_reqs == 0) return PKV_OK;
+  AllocArgs a = alloc_args(free_list, status);
+  a.B = batch->num_reqs;
+  a.cached_len = batch->cached_len;
+  a.device_len = batch->device_len;
+  a.alloc_rows = alloc_rows;
+  a.max_alloc = max_alloc;
+  hipError_t e = launch_alloc_pages(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : hip_failed(e);
+}
+
+int pkv_free_pages(const pkv_free_list* free_list, const int32_t* rows, int32_t num_rows, int32_t* status,
+                   void* stream) {
+  int rc = check_free_list(free_list);
+  if (rc != PKV_OK) return rc;
+  if (num_rows < 0 || (num_rows > 0 && !rows)) return PKV_ERR_INVALID_ARGUMENT;
+  if (num_rows == 0) return PKV_OK;
+  AllocArgs a = alloc_args(free_list, status);
+  a.free_rows = rows;
+  a.num_free = num_rows;
+  hipError_t e = launch_free_pages(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : hip_failed(e);
+}
+
 int pkv_rope_cos_sin_cache(float* cache, int32_t max_position, int32_t head_dim, double base, void* stream) {
   if (!cache || !aligned16(cache) || max_position <= 0) return PKV_ERR_INVALID_ARGUMENT;
   if (head_dim != kHeadDim) return PKV_ERR_UNSUPPORTED;

@@ -43,6 +43,24 @@ struct RopeCacheArgs {
   double log2_base;
 };
 
+struct AllocArgs {
+  int32_t* rows;              // ring of free page-start rows [capacity]
+  int32_t* state;             // [2]: head, count
+  int32_t capacity;
+  int32_t page_size;
+  int64_t num_pool_rows;
+  // allocation
+  int32_t B;
+  const int32_t* cached_len;
+  const int32_t* device_len;
+  int32_t* alloc_rows;
+  int64_t max_alloc;
+  // freeing
+  const int32_t* free_rows;
+  int32_t num_free;
+  int32_t* status;
+};
+
 struct MetaArgs {
   int32_t B, num_decode, R, W, page_shift, group;
   int64_t T, num_pool_rows, num_alloc;
@@ -90,6 +108,9 @@ int hip_failed(hipError_t e);
 
 hipError_t launch_kv_store(const StoreArgs& a, hipStream_t s);
 hipError_t launch_kv_store_rope(const RopeArgs& a, hipStream_t s);
+hipError_t launch_alloc_pages(const AllocArgs& a, hipStream_t s);
+hipError_t launch_free_pages(const AllocArgs& a, hipStream_t s);
+hipError_t launch_free_list_reset(int32_t* state, int32_t num_free, hipStream_t s);
 hipError_t launch_rope_cache(const RopeCacheArgs& a, hipStream_t s);
 hipError_t launch_metadata(const MetaArgs& a, hipStream_t s);
 hipError_t launch_decode(const AttnArgs& a, hipStream_t s);

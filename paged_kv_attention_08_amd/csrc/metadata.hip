@@ -175,7 +175,16 @@ __global__ void __launch_bounds__(256) token_kernel(MetaArgs a) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= a.T) return;
   const int32_t* alloc_ptr = (const int32_t*)(a.plan + a.layout.alloc_ptr_off);
-  if (t >= a.qo_indptr[a.B]) return;  // fewer new tokens than num_tokens (flagged by plan_kernel)
+  // A token that gets no row is marked -1 in out_loc and positions, so the
+  // store and RoPE calls skip it instead of reusing a stale row.
+  auto unmapped = [&]() {
+    a.out_loc[t] = -1;
+    a.positions[t] = -1;
+  };
+  if (t >= a.qo_indptr[a.B]) {  // fewer new tokens than num_tokens (flagged by plan_kernel)
+    unmapped();
+    return;
+  }
   // request i: qo_indptr[i] <= t < qo_indptr[i + 1]
   int lo = 0, hi = a.B;
   while (hi - lo > 1) {
@@ -185,7 +194,10 @@ __global__ void __launch_bounds__(256) token_kernel(MetaArgs a) {
   }
   const int i = lo;
   int32_t bits = 0;
-  if (!request_ok(a, i, &bits)) return;  // already reported by plan_kernel
+  if (!request_ok(a, i, &bits)) {  // already reported by plan_kernel
+    unmapped();
+    return;
+  }
   const int32_t r = a.table_idx[i];
   const int32_t c = a.cached_len[i];
   const int32_t j = c + (int32_t)(t - a.qo_indptr[i]);
@@ -212,6 +224,7 @@ __global__ void __launch_bounds__(256) token_kernel(MetaArgs a) {
   }
   if (bits) {
     raise_status(a.status, bits);
+    unmapped();
     return;
   }
   pt_row[j] = (int32_t)row;

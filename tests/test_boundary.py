@@ -241,3 +241,24 @@ def test_decode_graph_rejects_before_capture(lib):
         _lib.PKV_ERR_INVALID_ARGUMENT                     # the default stream cannot be captured
     assert lib.pkv_decode_graph_replay(None, 1, 1, None, FAKE) == _lib.PKV_ERR_INVALID_ARGUMENT
     assert lib.pkv_decode_graph_destroy(None) == _lib.PKV_ERR_INVALID_ARGUMENT
+
+
+def test_page_allocator_rejects(lib):
+    fl = _lib.FreeList(FAKE, FAKE, 64, 16, 4096)
+    b = batch()
+    assert lib.pkv_alloc_pages(None, B(b), FAKE, 8, None, None) == _lib.PKV_ERR_INVALID_ARGUMENT
+    assert lib.pkv_alloc_pages(B(_lib.FreeList(FAKE, FAKE, 64, 3, 4096)), B(b), FAKE, 8, None, None) == \
+        _lib.PKV_ERR_UNSUPPORTED
+    assert lib.pkv_alloc_pages(B(_lib.FreeList(FAKE, FAKE, 0, 16, 4096)), B(b), FAKE, 8, None, None) == \
+        _lib.PKV_ERR_INVALID_ARGUMENT
+    assert lib.pkv_alloc_pages(B(_lib.FreeList(FAKE, FAKE, 64, 16, 4095)), B(b), FAKE, 8, None, None) == \
+        _lib.PKV_ERR_INVALID_ARGUMENT
+    assert lib.pkv_alloc_pages(B(fl), B(b), None, 8, None, None) == _lib.PKV_ERR_INVALID_ARGUMENT
+    assert lib.pkv_alloc_pages(B(fl), B(b), FAKE, -1, None, None) == _lib.PKV_ERR_INVALID_ARGUMENT
+    assert lib.pkv_alloc_pages(B(fl), B(batch(num_reqs=0, num_decode=0, num_tokens=0)), None, 0, None, None) == \
+        _lib.PKV_OK                                        # empty batch: nothing launched
+    assert lib.pkv_free_pages(B(fl), None, 4, None, None) == _lib.PKV_ERR_INVALID_ARGUMENT
+    assert lib.pkv_free_pages(B(fl), FAKE, -1, None, None) == _lib.PKV_ERR_INVALID_ARGUMENT
+    assert lib.pkv_free_pages(B(fl), None, 0, None, None) == _lib.PKV_OK
+    assert lib.pkv_free_list_reset(B(fl), 65, None) == _lib.PKV_ERR_INVALID_ARGUMENT
+    assert lib.pkv_free_list_reset(B(fl), -1, None) == _lib.PKV_ERR_INVALID_ARGUMENT
