@@ -210,6 +210,36 @@ int paged_extend_attn(const pkv_kv_pool* pool, const pkv_page_table* page_table,
                       const pkv_attn_metadata* meta, const void* q, void* o, int32_t num_qo_heads,
                       float sm_scale, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- all layers' KV cache in one buffer ------------------------------------ */
+
+/* The engine's KV cache (deep dive 6.2, MHAKVCache): one bf16 buffer holding K
+ * (index 0) and V (index 1) of every layer.  Two physical orders:
+ *   PKV_LAYOUT_LAYER_FIRST : [2][num_layers][num_rows][Hkv][head_dim]
+ *                            (a layer's rows are contiguous)
+ *   PKV_LAYOUT_PAGE_FIRST  : [2][num_rows][num_layers][Hkv][head_dim]
+ *                            (a row's layers are contiguous; the pages' permuted
+ *                            view has the same logical shape, but a layer's rows
+ *                            are num_layers * Hkv * head_dim elements apart)
+ * Every call works on one layer's pkv_kv_pool, obtained with pkv_kv_cache_layer. */
+#define PKV_LAYOUT_LAYER_FIRST 0
+#define PKV_LAYOUT_PAGE_FIRST  1
+
+typedef struct pkv_kv_cache {
+  void* data;              /* device, 16-byte aligned */
+  int64_t num_rows;        /* pages * page_size, < 2^31 */
+  int32_t num_layers;      /* > 0 */
+  int32_t layout;          /* PKV_LAYOUT_* */
+  int32_t page_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t reserved;        /* must be 0 */
+} pkv_kv_cache;
+
+/* pkv_kv_cache_layer: fills *pool (host struct) with layer layer_id's K and V
+ * base pointers and row stride (the forward pass's layer_id, deep dive 5.1).
+ * Host only; launches nothing. */
+int pkv_kv_cache_layer(const pkv_kv_cache* cache, int32_t layer_id, pkv_kv_pool* pool);
+
 /* ---- rotary position embedding fused into the store ----------------------- */
 
 /* Optional RMS norm of every q and k head row before the rotation (deep dive

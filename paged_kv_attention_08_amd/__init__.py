@@ -22,7 +22,7 @@ from ._lib import (PKV_STATUS_BAD_ALLOC, PKV_STATUS_BAD_DECODE, PKV_STATUS_BAD_L
                    PKV_STATUS_BAD_PAGE_ROW, PKV_STATUS_BAD_POSITION, PKV_STATUS_BAD_TABLE_IDX,
                    PKV_STATUS_FREE_OVERFLOW, PKV_STATUS_OUT_OF_PAGES, PKV_STATUS_TOKEN_COUNT)
 
-__all__ = ["PagedKVError", "KVPoolTensors", "BatchTensors", "MetadataBuffers", "kv_store", "build_attn_metadata",
+__all__ = ["PagedKVError", "KVPoolTensors", "KVCacheTensors", "BatchTensors", "MetadataBuffers", "kv_store", "build_attn_metadata",
            "paged_decode_attn", "paged_extend_attn", "plan_bytes", "workspace_bytes", "library_path",
            "rope_cos_sin_cache", "kv_store_rope", "PKV_STATUS_BAD_POSITION", "DecodeGraph", "PageFreeList",
            "PKV_STATUS_OUT_OF_PAGES", "PKV_STATUS_FREE_OVERFLOW",
@@ -89,6 +89,45 @@ class KVPoolTensors:
         if self.k.stride(2) != 1 or self.k.stride(1) != d:
             raise ValueError("each pool row's heads must be contiguous")
         return _lib.KVPool(self.k.data_ptr(), self.v.data_ptr(), n, self.k.stride(0), self.page_size, hkv, d, 0)
+
+
+class KVCacheTensors:
+    """All layers' K and V in one bf16 buffer, in the engine's layer-first
+    ([2, L, N, Hkv, d]) or page-first ([2, N, L, Hkv, d]) physical order;
+    layer(i) is that layer's pool for the four calls."""
+
+    LAYER_FIRST = _lib.PKV_LAYOUT_LAYER_FIRST
+    PAGE_FIRST = _lib.PKV_LAYOUT_PAGE_FIRST
+
+    def __init__(self, num_layers: int, num_rows: int, num_kv_heads: int, head_dim: int = 128, page_size: int = 1,
+                 layout: int = _lib.PKV_LAYOUT_LAYER_FIRST, device="cuda"):
+        shape = ((2, num_layers, num_rows, num_kv_heads, head_dim) if layout == self.LAYER_FIRST
+                 else (2, num_rows, num_layers, num_kv_heads, head_dim))
+        self.data = torch.zeros(shape, dtype=torch.bfloat16, device=device)
+        self.num_layers, self.num_rows, self.layout = num_layers, num_rows, layout
+        self.num_kv_heads, self.head_dim, self.page_size = num_kv_heads, head_dim, page_size
+
+    def struct(self) -> _lib.KVCache:
+        return _lib.KVCache(self.data.data_ptr(), self.num_rows, self.num_layers, self.layout, self.page_size,
+                            self.num_kv_heads, self.head_dim, 0)
+
+    def layer_struct(self, layer_id: int) -> _lib.KVPool:
+        """The library's description of one layer (base pointers, row stride)."""
+        c, p = self.struct(), _lib.KVPool()
+        _check("pkv_kv_cache_layer", _lib.lib().pkv_kv_cache_layer(ctypes.byref(c), layer_id, ctypes.byref(p)))
+        return p
+
+    def layer(self, layer_id: int) -> "KVPoolTensors":
+        """Views of one layer's K and V rows; their struct() equals layer_struct()."""
+        if self.layout == self.LAYER_FIRST:
+            k, v = self.data[0, layer_id], self.data[1, layer_id]
+        else:
+            k, v = self.data[0, :, layer_id], self.data[1, :, layer_id]
+        pool = KVPoolTensors(k, v, self.page_size)
+        want, got = self.layer_struct(layer_id), pool.struct()
+        if (want.k, want.v, want.row_stride) != (got.k, got.v, got.row_stride):
+            raise AssertionError("layer view and library layer description differ")
+        return pool
 
 
 @dataclass

@@ -47,6 +47,15 @@ class AttnMetadata(ctypes.Structure):
                 ("plan_bytes", c_size_t), ("status", c_void_p)]
 
 
+PKV_LAYOUT_LAYER_FIRST = 0
+PKV_LAYOUT_PAGE_FIRST = 1
+
+
+class KVCache(ctypes.Structure):
+    _fields_ = [("data", c_void_p), ("num_rows", c_int64), ("num_layers", c_int32), ("layout", c_int32),
+                ("page_size", c_int32), ("num_kv_heads", c_int32), ("head_dim", c_int32), ("reserved", c_int32)]
+
+
 class QKNorm(ctypes.Structure):
     _fields_ = [("q_weight", c_void_p), ("k_weight", c_void_p), ("eps", c_float), ("reserved", c_int32)]
 
@@ -75,6 +84,7 @@ PROTOTYPES = {
                                   c_void_p, c_void_p, c_int32, c_float, c_void_p, c_size_t, c_void_p]),
     "paged_extend_attn": (c_int, [POINTER(KVPool), POINTER(PageTable), POINTER(Batch), POINTER(AttnMetadata),
                                   c_void_p, c_void_p, c_int32, c_float, c_void_p, c_size_t, c_void_p]),
+    "pkv_kv_cache_layer": (c_int, [POINTER(KVCache), c_int32, POINTER(KVPool)]),
     "pkv_rope_cos_sin_cache": (c_int, [c_void_p, c_int32, c_int32, ctypes.c_double, c_void_p]),
     "kv_store_rope": (c_int, [POINTER(KVPool), c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int64,
                               c_void_p, c_int32, POINTER(QKNorm), c_void_p, c_void_p]),

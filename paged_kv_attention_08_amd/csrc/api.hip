@@ -285,6 +285,39 @@ int pkv_free_pages(const pkv_free_list* free_list, const int32_t* rows, int32_t 
   return e == hipSuccess ? PKV_OK : hip_failed(e);
 }
 
+int pkv_kv_cache_layer(const pkv_kv_cache* cache, int32_t layer_id, pkv_kv_pool* pool) {
+  if (!cache || !pool || !cache->data || !aligned16(cache->data) || cache->reserved != 0) return PKV_ERR_INVALID_ARGUMENT;
+  if (cache->num_layers <= 0 || layer_id < 0 || layer_id >= cache->num_layers) return PKV_ERR_INVALID_ARGUMENT;
+  if (cache->layout != PKV_LAYOUT_LAYER_FIRST && cache->layout != PKV_LAYOUT_PAGE_FIRST) return PKV_ERR_INVALID_ARGUMENT;
+  if (cache->head_dim != kHeadDim) return PKV_ERR_UNSUPPORTED;
+  if (cache->num_kv_heads <= 0 || cache->num_rows <= 0) return PKV_ERR_INVALID_ARGUMENT;
+  const int64_t row = (int64_t)cache->num_kv_heads * cache->head_dim;  // elements of one layer's row
+  const int64_t L = cache->num_layers, N = cache->num_rows;
+  int64_t k_off, v_off, stride;
+  if (cache->layout == PKV_LAYOUT_LAYER_FIRST) {
+    k_off = (int64_t)layer_id * N * row;
+    v_off = (L + layer_id) * N * row;
+    stride = row;
+  } else {
+    k_off = (int64_t)layer_id * row;
+    v_off = N * L * row + (int64_t)layer_id * row;
+    stride = L * row;
+  }
+  pkv_kv_pool p;
+  p.k = static_cast<uint16_t*>(cache->data) + k_off;
+  p.v = static_cast<uint16_t*>(cache->data) + v_off;
+  p.num_rows = N;
+  p.row_stride = stride;
+  p.page_size = cache->page_size;
+  p.num_kv_heads = cache->num_kv_heads;
+  p.head_dim = cache->head_dim;
+  p.reserved = 0;
+  const int rc = check_pool(&p);  // page size, row count and stride limits
+  if (rc != PKV_OK) return rc;
+  *pool = p;
+  return PKV_OK;
+}
+
 int pkv_rope_cos_sin_cache(float* cache, int32_t max_position, int32_t head_dim, double base, void* stream) {
   if (!cache || !aligned16(cache) || max_position <= 0) return PKV_ERR_INVALID_ARGUMENT;
   if (head_dim != kHeadDim) return PKV_ERR_UNSUPPORTED;

@@ -31,12 +31,19 @@ def i32(a, device) -> torch.Tensor:
 class DeviceStep:
     """All device buffers of one batch of one layer, plus the four calls."""
 
-    def __init__(self, w, device="cuda", o_fill_nan: bool = True, upload_chunk_rows: int = 1 << 18):
+    def __init__(self, w, device="cuda", o_fill_nan: bool = True, upload_chunk_rows: int = 1 << 18,
+                 pool: "pkv.KVPoolTensors" = None):
+        """pool: an existing (zeroed) pool view to fill, e.g. one layer of a
+        multi-layer cache; by default a fresh pool is allocated."""
         self.w = w
         self.device = device
         N, Hkv, d = w.num_pool_rows, w.num_kv_heads, w.head_dim
-        self.k_pool = torch.zeros((N, Hkv, d), dtype=torch.bfloat16, device=device)
-        self.v_pool = torch.zeros((N, Hkv, d), dtype=torch.bfloat16, device=device)
+        if pool is None:
+            self.k_pool = torch.zeros((N, Hkv, d), dtype=torch.bfloat16, device=device)
+            self.v_pool = torch.zeros((N, Hkv, d), dtype=torch.bfloat16, device=device)
+        else:
+            assert tuple(pool.k.shape) == (N, Hkv, d) and pool.page_size == w.page_size
+            self.k_pool, self.v_pool = pool.k, pool.v
         rows = w.cached_rows
         for s in range(0, rows.size, upload_chunk_rows):
             r = torch.from_numpy(rows[s:s + upload_chunk_rows]).to(device)

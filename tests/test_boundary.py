@@ -262,3 +262,31 @@ def test_page_allocator_rejects(lib):
     assert lib.pkv_free_pages(B(fl), None, 0, None, None) == _lib.PKV_OK
     assert lib.pkv_free_list_reset(B(fl), 65, None) == _lib.PKV_ERR_INVALID_ARGUMENT
     assert lib.pkv_free_list_reset(B(fl), -1, None) == _lib.PKV_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("layout", [_lib.PKV_LAYOUT_LAYER_FIRST, _lib.PKV_LAYOUT_PAGE_FIRST])
+def test_kv_cache_layer_pointers(lib, layout):
+    """Host-only pointer arithmetic of the multi-layer cache (nothing launched)."""
+    base, L, N, hkv, d = 1 << 20, 3, 4096, 8, 128
+    row = hkv * d
+    c = _lib.KVCache(base, N, L, layout, 16, hkv, d, 0)
+    for layer in range(L):
+        p = _lib.KVPool()
+        assert lib.pkv_kv_cache_layer(B(c), layer, B(p)) == _lib.PKV_OK
+        if layout == _lib.PKV_LAYOUT_LAYER_FIRST:
+            k_elem, v_elem, stride = layer * N * row, (L + layer) * N * row, row
+        else:
+            k_elem, v_elem, stride = layer * row, N * L * row + layer * row, L * row
+        assert (p.k, p.v, p.row_stride) == (base + 2 * k_elem, base + 2 * v_elem, stride)
+        assert (p.num_rows, p.page_size, p.num_kv_heads, p.head_dim) == (N, 16, hkv, d)
+    p = _lib.KVPool()
+    assert lib.pkv_kv_cache_layer(B(c), L, B(p)) == _lib.PKV_ERR_INVALID_ARGUMENT
+    assert lib.pkv_kv_cache_layer(B(c), -1, B(p)) == _lib.PKV_ERR_INVALID_ARGUMENT
+    assert lib.pkv_kv_cache_layer(B(_lib.KVCache(base, N, L, 2, 16, hkv, d, 0)), 0, B(p)) == \
+        _lib.PKV_ERR_INVALID_ARGUMENT
+    assert lib.pkv_kv_cache_layer(B(_lib.KVCache(base, N, L, layout, 16, hkv, 64, 0)), 0, B(p)) == \
+        _lib.PKV_ERR_UNSUPPORTED
+    assert lib.pkv_kv_cache_layer(B(_lib.KVCache(base, N, L, layout, 3, hkv, d, 0)), 0, B(p)) == \
+        _lib.PKV_ERR_UNSUPPORTED
+    assert lib.pkv_kv_cache_layer(B(_lib.KVCache(base + 8, N, L, layout, 16, hkv, d, 0)), 0, B(p)) == \
+        _lib.PKV_ERR_INVALID_ARGUMENT
