@@ -138,6 +138,43 @@ def graph_measurement(ds, w, args, stream):
             "what": "build_attn_metadata + kv_store + paged_decode_attn, eager launches vs one graph replay"}
 
 
+def alloc_measurement(ds, w, args, stream):
+    """pkv_alloc_pages for the step's batch from a free list holding every
+    page of the pool, then pkv_free_pages of the same pages: one pair per
+    step, timed back to back."""
+    import torch
+    import paged_kv_attention_08_amd as pkv
+
+    s = w.page_size
+    npages = w.num_pool_rows // s
+    fl = pkv.PageFreeList(npages, s, w.num_pool_rows)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    fl.reset((torch.randperm(npages, device="cuda", generator=g, dtype=torch.int64) * s).to(torch.int32))
+    c, d = w.cached_len.astype(np.int64), w.device_len.astype(np.int64)
+    ok = (c >= 0) & (c <= d)
+    n = int((((d + s - 1) // s) - ((c + s - 1) // s))[ok].sum())
+    alloc = torch.empty(max(n, 1), dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def pair():
+        fl.alloc(ds.batch, alloc, status, stream)
+        fl.free(alloc[:n], status, stream)
+
+    for _ in range(args.warmup):
+        pair()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        pair()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, f"allocator status {int(status.item()):#x}"
+    return {"pages_per_step": n, "free_list_pages": npages,
+            "alloc_plus_free_ms": round(ev[0].elapsed_time(ev[1]) / args.steps, 4),
+            "what": "pkv_alloc_pages + pkv_free_pages of the step's new pages (launch-latency bound)"}
+
+
 def rope_measurement(ds, w, args, stream, PM):
     """kv_store_rope (RoPE with Qwen3-style per-head q/k RMS norm, base 1e6) on
     the step's tokens at their metadata positions and rows; timed on its own,
@@ -186,6 +223,9 @@ def main(argv=None):
     ap.add_argument("--flush", action="store_true", help="flush L2/MALL before every step (outside the events)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layout", choices=["layer_first", "page_first"], default="layer_first",
+                    help="physical order of a multi-layer KV cache whose layer 0 the step runs on")
+    ap.add_argument("--layers", type=int, default=1, help="layers in that cache (1: a plain one-layer pool)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (torch copy_) 5 times: the known-size reference "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
@@ -219,7 +259,13 @@ def main(argv=None):
     log(f"generating config {args.config}")
     w = configs.FULL[args.config]()
     log(w.summary())
-    ds = DeviceStep(w)
+    pool = None
+    if args.layers > 1 or args.layout != "layer_first":
+        import paged_kv_attention_08_amd as pkv
+        layout = pkv.KVCacheTensors.PAGE_FIRST if args.layout == "page_first" else pkv.KVCacheTensors.LAYER_FIRST
+        cache = pkv.KVCacheTensors(args.layers, w.num_pool_rows, w.num_kv_heads, w.head_dim, w.page_size, layout)
+        pool = cache.layer(0)
+    ds = DeviceStep(w, pool=pool)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda") if args.flush else None
@@ -309,7 +355,8 @@ def main(argv=None):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.config], "config_index": args.config,
                    "global_batch": w.num_reqs, "new_tokens": w.num_tokens, "parallelism": "single GPU",
-                   "l2_mall_flush_between_steps": bool(args.flush)},
+                   "l2_mall_flush_between_steps": bool(args.flush),
+                   "kv_cache": f"{args.layers} layer(s), {args.layout}, step on layer 0"},
         "breakdown_ms": {"metadata": round(float(mean_ms[0]), 4), "kv_store": round(float(mean_ms[1]), 4),
                          "decode": round(float(mean_ms[2]), 4), "extend": round(float(mean_ms[3]), 4),
                          "wall_per_step": round(wall_ms, 4), "events_per_step": round(step_ms, 4)},
@@ -323,6 +370,7 @@ def main(argv=None):
     out["next_rows"] = {}
     if has_decode and not has_extend:
         out["next_rows"]["decode_graph"] = graph_measurement(ds, w, args, stream)
+    out["next_rows"]["page_alloc"] = alloc_measurement(ds, w, args, stream)
     out["next_rows"]["kv_store_rope"] = rope_measurement(ds, w, args, stream, PM)
     ds.free()
     if not args.no_cpu_baseline:
