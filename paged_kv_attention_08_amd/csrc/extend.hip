@@ -55,6 +55,8 @@ constexpr int kKsStride = 136;  // bf16 elements per K row in LDS (128 + 8 pad)
 constexpr int kVsStride = 160;  // bf16 elements per V row in LDS (80 dwords: 4 rows x 16 dwords hit 64 distinct banks)
 constexpr int kWaves = 8;
 static_assert(kExtendRows == 32 * kWaves, "one 32-row block per wavefront");
+constexpr int kWaveKeys = kKeyTile / kWaves;  // keys of a tile one wavefront gathers
+constexpr int kLoads = kWaveKeys / 4;         // 16-byte loads per lane per tile and per K / V (4 rows per load)
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 
@@ -65,7 +67,7 @@ __device__ inline float dot2_bf16(uint32_t w, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w), __builtin_bit_cast(bf16x2v, 0x3F803F80u), acc, false);
 }
 
-__global__ void __launch_bounds__(512, 1) extend_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(64 * kWaves, 8 / kWaves) extend_kernel(AttnArgs a) {
   // two LDS stages: tile n lives in stage n % 2
   __shared__ __attribute__((aligned(16))) uint16_t ks_all[2][kKeyTile * kKsStride];
   __shared__ __attribute__((aligned(16))) uint16_t vs_all[2][kKeyTile * kVsStride];
@@ -122,39 +124,45 @@ __global__ void __launch_bounds__(512, 1) extend_kernel(AttnArgs a) {
   const uint32_t row_elems = (uint32_t)a.row_stride;  // < 2^31, checked on the host
   const uint32_t n_rows = (uint32_t)a.num_pool_rows;
 
-  // loader: load u (0..1) of lane l in wavefront w moves 16 bytes (dims
-  // 8 (l % 16) ..) of key 8 w + 4 u + l / 16 of the tile.  Keys past kv_end
+  // loader: load u (0..kLoads-1) of lane l in wavefront w moves 16 bytes
+  // (dims 8 (l % 16) ..) of key kWaveKeys w + 4 u + l / 16 of the tile.  Keys past kv_end
   // re-read the last valid key's row (masked, V zeroed).
-  uint4 kpre[2][2], vpre[2][2];  // [register set][load]
+  uint4 kpre[2][kLoads], vpre[2][kLoads];  // [register set][load]
   // page-table entries of the next tile to gather, one per load (16 lanes share one)
-  int32_t ent[2];
+  int32_t ent[kLoads];
   auto load_entries = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) ent[u] = pt_row[min(kt + 8 * wave + 4 * u + (lane >> 4), kv_end - 1)];
+    for (int u = 0; u < kLoads; ++u) ent[u] = pt_row[min(kt + kWaveKeys * wave + 4 * u + (lane >> 4), kv_end - 1)];
   };
   auto gather = [&](int kt, auto set_tag) __attribute__((always_inline)) {
     constexpr int SET = decltype(set_tag)::value;
-    uint32_t r0 = (uint32_t)ent[0], r1 = (uint32_t)ent[1];
-    const bool b0 = r0 >= n_rows, b1 = r1 >= n_rows;  // also catches negative entries
-    r0 = b0 ? 0u : r0;
-    r1 = b1 ? 0u : r1;
+    uint32_t r[kLoads];
+    bool bad = false;
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+      r[u] = (uint32_t)ent[u];
+      const bool b = r[u] >= n_rows;  // also catches negative entries
+      bad |= b;
+      r[u] = b ? 0u : r[u];
+    }
     // the next tile's entries are requested before this tile's rows, so the
     // wait for them (one tile later) can leave these row loads in flight
     load_entries(kt + kKeyTile);
     // 32 x 32 -> 64-bit row offsets
-    const uint64_t off0 = (uint64_t)r0 * row_elems, off1 = (uint64_t)r1 * row_elems;
-    kpre[SET][0] = load16(kbase + off0);
-    vpre[SET][0] = load16(vbase + off0);
-    kpre[SET][1] = load16(kbase + off1);
-    vpre[SET][1] = load16(vbase + off1);
-    if (b0 || b1) raise_status(a.status, PKV_STATUS_BAD_PAGE_ROW);
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+      const uint64_t off = (uint64_t)r[u] * row_elems;
+      kpre[SET][u] = load16(kbase + off);
+      vpre[SET][u] = load16(vbase + off);
+    }
+    if (bad) raise_status(a.status, PKV_STATUS_BAD_PAGE_ROW);
   };
   auto zero_tail = [&](int kt, auto set_tag) __attribute__((always_inline)) {
     constexpr int SET = decltype(set_tag)::value;
     if (kt + kKeyTile > kv_end) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-        if (kt + 8 * wave + 4 * u + (lane >> 4) >= kv_end) vpre[SET][u] = make_uint4(0, 0, 0, 0);
+      for (int u = 0; u < kLoads; ++u)
+        if (kt + kWaveKeys * wave + 4 * u + (lane >> 4) >= kv_end) vpre[SET][u] = make_uint4(0, 0, 0, 0);
     }
   };
 
@@ -175,8 +183,8 @@ __global__ void __launch_bounds__(512, 1) extend_kernel(AttnArgs a) {
     constexpr int S = decltype(set_tag)::value;
     zero_tail(kt, set_tag);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int key = 8 * wave + 4 * u + (lane >> 4);
+    for (int u = 0; u < kLoads; ++u) {
+      const int key = kWaveKeys * wave + 4 * u + (lane >> 4);
       *reinterpret_cast<uint4*>(&ks_all[S][key * kKsStride + (lane & 15) * 8]) = kpre[S][u];
       *reinterpret_cast<uint4*>(&vs_all[S][key * kVsStride + (lane & 15) * 8]) = vpre[S][u];
     }
