@@ -147,7 +147,9 @@ size_t paged_attn_workspace_bytes(int32_t max_reqs, int32_t num_qo_heads, int32_
  *   out_loc      : int32 [num_tokens]
  * Tokens with the same target row (only padding tokens on the dummy page)
  * race: that row ends up holding one of them, possibly mixed.  A token whose
- * out_loc is outside the pool is skipped (PKV_STATUS_BAD_OUT_LOC).
+ * out_loc is outside the pool is skipped (PKV_STATUS_BAD_OUT_LOC), except -1,
+ * build_attn_metadata's mark for a token it could not map, which is skipped
+ * silently (the cause is already reported).
  * num_tokens == 0 is a no-op. */
 int kv_store(const pkv_kv_pool* pool, const void* k_new, const void* v_new, const int32_t* out_loc,
              int64_t num_tokens, int32_t* status, void* stream);
@@ -280,7 +282,8 @@ int pkv_rope_cos_sin_cache(float* cache, int32_t max_position, int32_t head_dim,
  * All rows 16-byte aligned and contiguous.  A token whose position is outside
  * [0, max_position) is left entirely untouched (PKV_STATUS_BAD_POSITION); one
  * whose out_loc is outside the pool has q rotated but nothing stored
- * (PKV_STATUS_BAD_OUT_LOC).  Tokens sharing a target row race as in kv_store.
+ * (PKV_STATUS_BAD_OUT_LOC).  A position or out_loc of -1 (an unmapped token)
+ * is skipped the same way without raising a bit.  Tokens sharing a target row race as in kv_store.
  * num_tokens == 0 is a no-op. */
 int kv_store_rope(const pkv_kv_pool* pool, void* q, int32_t num_qo_heads, const void* k_new, const void* v_new,
                   const int32_t* out_loc, const int32_t* positions, int64_t num_tokens,

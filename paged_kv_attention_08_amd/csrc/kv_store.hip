@@ -20,7 +20,8 @@ __global__ void __launch_bounds__(256) kv_store_kernel(StoreArgs a) {
     const int32_t c = (int32_t)(idx - t * a.row_vec);
     const int32_t row = a.out_loc[t];
     if (row < 0 || (int64_t)row >= a.num_rows) {
-      if (c == 0) raise_status(a.status, PKV_STATUS_BAD_OUT_LOC);
+      // -1 marks a token build_attn_metadata could not map (already reported)
+      if (c == 0 && row != -1) raise_status(a.status, PKV_STATUS_BAD_OUT_LOC);
       continue;
     }
     const int64_t dst = (int64_t)row * a.row_stride_vec + c;

@@ -34,13 +34,14 @@ __global__ void __launch_bounds__(256) kv_store_rope_kernel(RopeArgs a) {
   const int nrows = a.Hq + 2 * a.Hkv;
   for (int64_t t = blockIdx.x; t < a.num_tokens; t += gridDim.x) {
     const int32_t pos = a.positions[t];
+    // -1 marks a token build_attn_metadata could not map (already reported)
     if (pos < 0 || pos >= a.max_position) {
-      if (threadIdx.x == 0) raise_status(a.status, PKV_STATUS_BAD_POSITION);
+      if (threadIdx.x == 0 && pos != -1) raise_status(a.status, PKV_STATUS_BAD_POSITION);
       continue;  // uniform for the workgroup
     }
     const int32_t loc = a.out_loc[t];
     const bool store = loc >= 0 && (int64_t)loc < a.num_rows;
-    if (!store && threadIdx.x == 0) raise_status(a.status, PKV_STATUS_BAD_OUT_LOC);
+    if (!store && threadIdx.x == 0 && loc != -1) raise_status(a.status, PKV_STATUS_BAD_OUT_LOC);
     const float* cs = a.cos_sin + (int64_t)pos * kHeadDim;
     const float4 c4 = *reinterpret_cast<const float4*>(cs + 4 * lane16);
     const float4 s4 = *reinterpret_cast<const float4*>(cs + kHeadDim / 2 + 4 * lane16);

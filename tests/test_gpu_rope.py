@@ -117,7 +117,7 @@ def test_kv_store_rope_bad_position_and_row():
     T, hq, hkv = 8, 8, 8
     inp = rope_inputs(29, T, hq, hkv, max_position=1024)
     inp.positions[2] = 1024          # past the table: token untouched
-    inp.positions[3] = -1
+    inp.positions[3] = -7
     inp.out_loc[5] = inp.num_pool_rows  # outside the pool: q rotated, nothing stored
     q, k_pool, v_pool, st = run_rope(inp, hq, hkv, 1e4, False)
     assert st == (pkv.PKV_STATUS_BAD_POSITION | pkv.PKV_STATUS_BAD_OUT_LOC)
@@ -130,6 +130,19 @@ def test_kv_store_rope_bad_position_and_row():
         assert np.array_equal(bits(v_pool[r]), inp.v[t])
     for t in (2, 3):
         assert not bits(v_pool[int(inp.out_loc[t])]).any()
+
+
+def test_kv_store_rope_skips_unmapped_tokens_silently():
+    """-1 in positions / out_loc (tokens build_attn_metadata could not map) are
+    skipped without a status bit."""
+    T, hq, hkv = 6, 8, 8
+    inp = rope_inputs(31, T, hq, hkv, max_position=1024)
+    inp.positions[1] = -1
+    inp.out_loc[4] = -1
+    q, k_pool, v_pool, st = run_rope(inp, hq, hkv, 1e4, False)
+    assert st == 0
+    assert np.array_equal(bits(q)[1], inp.q[1])
+    assert not bits(v_pool[int(inp.out_loc[1])]).any()
 
 
 @pytest.mark.parametrize("cfg", [2, 3])
