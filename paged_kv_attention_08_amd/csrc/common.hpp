@@ -16,7 +16,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kHeadDim = 128;
 constexpr int kMaxGroup = 16;            // query heads per KV head handled by one MFMA column block
-constexpr int kDecodeTargetItems = 1024; // decode split-K items the plan aims for (see plan_kernel)
+constexpr int kDecodeTargetItems = 768;  // decode split-K items the plan aims for (see plan_kernel)
 constexpr int kExtendRows = 256;         // (token, query-head) rows per extend workgroup
 constexpr int kPlanHeaderInts = 16;
 
