@@ -19,7 +19,7 @@ namespace pkv {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;
 
 __device__ inline int32_t pages_for(int32_t c, int32_t d, int32_t s) {
   if (c < 0 || c > d) return 0;  // invalid lengths need no page (build_attn_metadata counts the same way)
@@ -52,6 +52,7 @@ __global__ void __launch_bounds__(kThreads) alloc_pages_kernel(AllocArgs a) {
     return;
   }
   int bad = 0;
+#pragma unroll 4
   for (long long j = threadIdx.x; j < need; j += kThreads) {
     long long idx = head + j;
     if (idx >= a.capacity) idx -= a.capacity;
@@ -83,6 +84,7 @@ __global__ void __launch_bounds__(kThreads) free_pages_kernel(AllocArgs a) {
     if (threadIdx.x == 0) raise_status(a.status, bad ? PKV_STATUS_BAD_ALLOC : PKV_STATUS_FREE_OVERFLOW);
     return;  // nothing freed
   }
+#pragma unroll 4
   for (int j = threadIdx.x; j < a.num_free; j += kThreads) {
     long long idx = (long long)head + count + j;
     if (idx >= a.capacity) idx -= a.capacity;
