@@ -336,7 +336,7 @@ def main(argv=None):
         roof = {"bound": "hbm", "achieved": round(decode_gbps, 1), "peak": PM.HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(decode_gbps / PM.HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                "kernel": "paged_decode_attn (decode_partial_kernel + decode_merge_kernel)",
+                "kernel": "paged_decode_attn (decode_kernel + decode_merge_kernel)",
                 "algorithmic_bytes_per_launch": dec_bytes, "avg_launch_ms": round(float(mean_ms[2]), 4),
                 "profile": None if measured is None else measured["summary"]}
     else:
