@@ -132,9 +132,10 @@ typedef struct pkv_attn_metadata {
  * max_tokens new tokens with these head counts.  0 on invalid arguments. */
 size_t pkv_plan_bytes(int32_t max_reqs, int64_t max_tokens, int32_t num_qo_heads, int32_t num_kv_heads);
 
-/* Bytes of the workspace paged_decode_attn needs for at most max_reqs
- * requests (the split-K partial results: fp32 accumulators plus running max
- * and sum per split and query head).  0 on invalid arguments. */
+/* Bytes of the workspace paged_decode_attn needs (the split-K partial
+ * results: fp32 accumulators plus running max and sum of the pieces of
+ * requests that several runs of wavefronts share).  It does not depend on max_reqs
+ * (kept for the ABI): about 34 MB at most.  0 on invalid arguments. */
 size_t paged_attn_workspace_bytes(int32_t max_reqs, int32_t num_qo_heads, int32_t head_dim);
 
 /* ---- entry points ------------------------------------------------------- */
@@ -187,8 +188,9 @@ int build_attn_metadata(const pkv_batch* batch, const pkv_page_table* page_table
  * over rows = page_table[table_idx[i], 0 .. device_len[i]) (the new row stored
  * by kv_store included), gathered through the page table.  Split-K
  * ("parallelise across KV", learning notes kernel passage; flash-decoding):
- * each plan item covers a key range of one request, and a merge kernel
- * combines the items' partial softmax states.
+ * the (request, group of KV heads, 32-key tile) work is split evenly over a
+ * fixed set of runs of wavefronts, so a request's keys may be shared by
+ * several of them, and a merge kernel combines their partial softmax states.
  *   q, o       : bf16 [num_tokens, Hq, head_dim]; rows of extend requests untouched
  *   workspace  : >= paged_attn_workspace_bytes(B, Hq, head_dim) bytes, 16-byte aligned
  * Must follow build_attn_metadata (same batch, head counts) and kv_store on

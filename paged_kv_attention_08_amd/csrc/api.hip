@@ -112,9 +112,10 @@ int fill_attn_args(const pkv_kv_pool* pool, const pkv_page_table* pt, const pkv_
   return PKV_OK;
 }
 
-size_t decode_ws_bytes(int32_t max_reqs, int32_t hq) {
-  const int64_t items = (int64_t)max_reqs + kDecodeTargetItems;
-  return (size_t)(items * hq * (kHeadDim + 2) * 4);
+// The decode kernel's partial states; G = Hq / Hkv is at most min(Hq, 16).
+size_t decode_ws_bytes(int32_t hq) {
+  const int32_t gmax = hq < kMaxGroup ? hq : kMaxGroup;
+  return (size_t)(decode_ws_floats(gmax) * 4);
 }
 
 }  // namespace
@@ -128,7 +129,7 @@ size_t pkv_plan_bytes(int32_t max_reqs, int64_t max_tokens, int32_t num_qo_heads
 
 size_t paged_attn_workspace_bytes(int32_t max_reqs, int32_t num_qo_heads, int32_t head_dim) {
   if (max_reqs < 0 || num_qo_heads <= 0 || head_dim != kHeadDim) return 0;
-  return decode_ws_bytes(max_reqs, num_qo_heads);
+  return decode_ws_bytes(num_qo_heads);
 }
 
 int kv_store(const pkv_kv_pool* pool, const void* k_new, const void* v_new, const int32_t* out_loc,
@@ -175,6 +176,7 @@ int build_attn_metadata(const pkv_batch* batch, const pkv_page_table* page_table
   a.W = page_table->width;
   a.page_shift = log2i(page_size);
   a.group = num_qo_heads / num_kv_heads;
+  a.Hkv = num_kv_heads;
   a.T = batch->num_tokens;
   a.num_pool_rows = num_pool_rows;
   a.num_alloc = num_alloc;
@@ -202,11 +204,11 @@ int paged_decode_attn(const pkv_kv_pool* pool, const pkv_page_table* page_table,
   int rc = fill_attn_args(pool, page_table, batch, meta, q, o, num_qo_heads, sm_scale, &a);
   if (rc != PKV_OK) return rc;
   if (batch->num_decode == 0) return PKV_OK;
-  const size_t need = decode_ws_bytes(batch->num_reqs, num_qo_heads);
+  const size_t need = decode_ws_bytes(num_qo_heads);
   if (!workspace || !aligned16(workspace)) return PKV_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < need) return PKV_ERR_WORKSPACE;
   a.ws_acc = static_cast<float*>(workspace);
-  a.ws_ml = a.ws_acc + (int64_t)a.layout.cap_items * num_qo_heads * kHeadDim;
+  a.ws_ml = a.ws_acc + (int64_t)kDecodeWaves * 2 * a.group * kHeadDim;
   hipError_t e = launch_decode(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : hip_failed(e);
 }

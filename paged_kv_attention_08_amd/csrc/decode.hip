@@ -6,17 +6,32 @@
 // sequence.  Deep dive 5.2: online softmax keeps a running max and sum so no
 // score vector is stored.
 //
-// Work decomposition (from the plan written by build_attn_metadata):
-//   item = (request, key range [k0, k1)); a workgroup of 4 wavefronts takes
-//   one item and 4 KV heads, one wavefront per KV head.  A wavefront walks its
-//   key range in tiles of 32 keys.
+// Work decomposition (from the plan written by build_attn_metadata): the
+// decode work is the flat sequence of (request, group of HG KV heads, 32-key
+// tile), request by request, each (request, group) "segment" holding
+// ceil(device_len / 32) tiles; HG is the largest of 8, 4, 2, 1 dividing Hkv.
+// A fixed set of kDecodeWaves / HG "runs" of HG wavefronts each (8 wavefronts
+// per workgroup, one workgroup per CU, all resident at once) take equal shares
+// of `per` consecutive tiles, so every run has the same work whatever the mix
+// of lengths (a per-request split into items of a fixed size left a quarter
+// of the wavefront slots idle on average at the serving-decode batch).  The
+// wavefronts of a run walk the same tiles, one KV head of the group each, so
+// at any time they read adjacent heads (2 KiB contiguous at HG = 8: whole K
+// and V rows of an 8-KV-head pool, measured 7% faster than 1 KiB pieces on
+// the serving-decode batch) of the same pool rows.  A wavefront walks its run
+// tile by tile across segment boundaries, keeping its loads in flight across
+// them; a segment that lies wholly inside the run is normalised and written
+// directly, and the piece of a segment shared with a neighbouring run is
+// published as a partial state.
 //
 // Per tile and wavefront (lane = 16 * grp + lo):
-//   * lanes 0..31 read the 32 page-table entries (requested two tiles ahead);
+//   * lanes 0..31 read the 32 page-table entries (requested two tiles ahead,
+//     possibly of the next segment);
 //     rows are broadcast with lane shuffles.  Each 16-lane group then loads
 //     one whole 256-byte head row of K and of V per instruction (4 rows per
-//     instruction, 8 + 8 loads per lane).  All loads are unconditional: a
-//     missing key reads pool row 0 and is masked.
+//     instruction, 8 + 8 loads per lane).  A missing key (past device_len)
+//     loads nothing and is masked: every key of a tile of a one-key padding
+//     request used to read pool row 0, and those loads piled onto one row.
 //   * software pipelining with one buffer: the tile's rows are written from
 //     registers to the wavefront's row-major K and V tiles in LDS, which frees
 //     the registers, and the next tile's loads are issued before this tile is
@@ -38,9 +53,11 @@
 //     barrier: each wavefront owns its tiles.
 // Merge ("wavefront-reduction softmax merge"): the four lane groups hold the
 // same running max, so a wavefront reduces its sums with two shuffles.  A
-// request covered by one item writes its output directly; otherwise every
-// item publishes its (acc, max, sum) to the workspace and a second launch
-// rescales the items of each request to their common max in one pass.
+// segment inside one run is written directly; otherwise each run publishes its
+// piece's (acc, max, sum) to the workspace (slot 0: the piece of the segment
+// the run started inside, slot 1: the one it ends inside) and a second launch
+// rescales the pieces of each (request, query head) to their common max in one
+// pass.
 // (Merging inside the first launch would need device-scope fences, which on
 // this chip write back and invalidate a whole L2 per workgroup; the launch
 // boundary orders the two kernels for free.)
@@ -50,8 +67,8 @@ namespace pkv {
 
 namespace {
 
-constexpr int kTileKeys = 32;
-constexpr int kWaves = kDecodeHeadsPerGroup;  // KV heads per workgroup (one per wavefront)
+constexpr int kTileKeys = kDecodeTileKeys;
+constexpr int kWaves = kDecodeWgWaves;  // wavefronts per workgroup: 8 / HG runs (no barrier between them)
 constexpr int kKsPitch = 136;  // bf16 per K row in LDS: 68 dwords, 16 rows x 4 dwords hit 64 distinct banks
 constexpr int kVsPitch = 144;  // bf16 per V row in LDS: 72 dwords, 8 rows x 8 dwords hit 64 distinct banks
 
@@ -69,48 +86,125 @@ __device__ inline u32x4 load16_stream(const uint16_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-__global__ void __launch_bounds__(256, 2) decode_kernel(AttnArgs a) {
+// Position in the flat decode order (uniform across the wavefront).
+struct Cursor {
+  int32_t i;    // request
+  int32_t g;    // group of KV heads
+  int32_t kti;  // tile within the segment
+  int32_t n;    // tiles per segment of request i
+  int32_t seg;  // flat index of the segment's first tile
+  int32_t dl;   // device_len of request i
+};
+
+__global__ void __launch_bounds__(64 * kWaves, 1) decode_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t ks[kWaves][kTileKeys * kKsPitch];
   __shared__ __attribute__((aligned(16))) uint16_t vs[kWaves][kTileKeys * kVsPitch];
 
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int lo = lane & 15;
   const int grp = lane >> 4;
   const int32_t* header = reinterpret_cast<const int32_t*>(a.plan);
-  const int item = blockIdx.x;
-  if (item >= header[0]) return;  // uniform for the workgroup
-  const int g = blockIdx.y * kWaves + wave;
-  if (g >= a.Hkv) return;  // no workgroup barrier below: idle wavefronts may leave
-
-  const int4 it = reinterpret_cast<const int4*>(a.plan + a.layout.items_off)[item];
-  const int i = it.x, k0 = it.y, k1 = it.z, nsplit = it.w;
+  const int32_t total = header[0];
+  const int32_t per = header[1];
+  const int Hkv = a.Hkv;
+  const int HG = decode_heads_per_group(Hkv);
+  const int Hg = Hkv / HG;
+  const int hw = wave % HG;  // this wavefront's KV head within the group
+  const int32_t run = blockIdx.x * (kWaves / HG) + wave / HG;
+  const int64_t f0l = (int64_t)run * per;
+  if (f0l >= total) return;  // uniform for the run; no workgroup barrier below
+  const int32_t f0 = (int32_t)f0l;
+  const int32_t f1 = (int32_t)min<int64_t>(f0l + per, total);
+  const int32_t* tptr = reinterpret_cast<const int32_t*>(a.plan + a.layout.dec_tiles_off);
   const int G = a.group;
-  const int64_t tok = a.qo_indptr[i];
-  if (tok < 0 || tok >= a.T) {
-    if (lane == 0) raise_status(a.status, PKV_STATUS_TOKEN_COUNT);
-    return;
+
+  // the request holding flat tile f0: Hg * tptr[i] <= f0 < Hg * tptr[i + 1]
+  Cursor cc;
+  {
+    int lo_i = 0, hi_i = a.num_decode;  // tptr[num_decode] * Hg = total > f0
+    while (hi_i - lo_i > 1) {
+      const int mid = (lo_i + hi_i) >> 1;
+      if ((int64_t)Hg * tptr[mid] <= f0) lo_i = mid;
+      else hi_i = mid;
+    }
+    cc.i = lo_i;
+    cc.n = tptr[lo_i + 1] - tptr[lo_i];
+    const int32_t local = f0 - Hg * tptr[lo_i];
+    cc.g = local / cc.n;
+    cc.kti = local - cc.g * cc.n;
+    cc.seg = Hg * tptr[lo_i] + cc.g * cc.n;
+    cc.dl = a.device_len[lo_i];
   }
-  const int32_t* pt_row = a.page_table + (int64_t)a.table_idx[i] * a.W;
-  // loader: load u (0..7) of lane l moves 16 bytes (dims 8 (l % 16) ..) of key
-  // 4 u + l / 16: each 16-lane group reads one whole 256-byte head row
-  const uint16_t* kbase = a.k_pool + (int64_t)g * kHeadDim + lo * 8;
-  const uint16_t* vbase = a.v_pool + (int64_t)g * kHeadDim + lo * 8;
-  const int64_t stride = a.row_stride;
+  // next tile of the flat order (only called while one exists in the run)
+  auto advance = [&](Cursor& c) __attribute__((always_inline)) {
+    if (++c.kti == c.n) {
+      c.kti = 0;
+      c.seg += c.n;
+      if (++c.g == Hg) {
+        c.g = 0;
+        do {
+          ++c.i;
+        } while (tptr[c.i + 1] == tptr[c.i]);  // requests without decode tiles
+        c.n = tptr[c.i + 1] - tptr[c.i];
+        c.dl = a.device_len[c.i];
+      }
+    }
+  };
+  auto token_of = [&](const Cursor& c) -> int64_t { return a.qo_indptr[c.i]; };
+  // this wavefront's KV head in c's group
+  auto head_of = [&](const Cursor& c) -> int { return c.g * HG + hw; };
+
   uint16_t* ktile = ks[wave];
   uint16_t* vtile = vs[wave];
+  const int64_t stride = a.row_stride;
 
   // B operand of S^T: the G query heads of KV head g (zero for padded columns)
-  bf16x8 qop[4];
-  {
-    const uint16_t* qrow = a.q + ((tok * a.Hq) + (int64_t)g * G + lo) * kHeadDim;
+  auto load_q = [&](const Cursor& c, bf16x8 (&qo)[4]) __attribute__((always_inline)) {
+    const int64_t tok = token_of(c);
+    const int h = head_of(c);
+    const bool ok = tok >= 0 && tok < a.T && lo < G;
+    const uint16_t* qrow = a.q + ((ok ? tok : 0) * a.Hq + (ok ? (int64_t)h * G + lo : 0)) * kHeadDim;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (lo < G) v = load16(qrow + (grp * 4 + kk) * 8);
-      qop[kk] = as_bf16x8(v);
+      if (ok) v = load16(qrow + (grp * 4 + kk) * 8);
+      qo[kk] = as_bf16x8(v);
     }
-  }
+  };
+  // Page-table entries of the 32 keys of c's tile: every lane loads (lanes
+  // 32..63 and keys past device_len re-read an in-range entry).
+  auto load_entries = [&](const Cursor& c) -> int32_t {
+    const int32_t* pt_row = a.page_table + (int64_t)a.table_idx[c.i] * a.W;
+    return pt_row[min(c.kti * kTileKeys + (lane & 31), c.dl - 1)];
+  };
+  // -1 marks a key past device_len or an entry outside the pool (reported)
+  auto check_entries = [&](const Cursor& c, int32_t e) -> int32_t {
+    const bool in_range = lane < kTileKeys && c.kti * kTileKeys + lane < c.dl;
+    if (in_range && (e < 0 || (int64_t)e >= a.num_pool_rows)) {
+      raise_status(a.status, PKV_STATUS_BAD_PAGE_ROW);
+      e = -1;
+    }
+    return in_range ? e : -1;
+  };
+  u32x4 kr[8], vr[8];  // the rows of the tile in flight
+  auto issue = [&](const Cursor& c, int32_t e) __attribute__((always_inline)) {
+    // loader: load u (0..7) of lane l moves 16 bytes (dims 8 (l % 16) ..) of
+    // key 4 u + l / 16: each 16-lane group reads one whole 256-byte head row
+    const int h = head_of(c);
+    const uint16_t* kbase = a.k_pool + (int64_t)h * kHeadDim + lo * 8;
+    const uint16_t* vbase = a.v_pool + (int64_t)h * kHeadDim + lo * 8;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int32_t row = __shfl(e, 4 * u + (lane >> 4), 64);
+      kr[u] = u32x4{0u, 0u, 0u, 0u};
+      vr[u] = u32x4{0u, 0u, 0u, 0u};
+      if (row >= 0) {  // the same for the 16 lanes of a group
+        kr[u] = load16_stream(kbase + (int64_t)row * stride);
+        vr[u] = load16_stream(vbase + (int64_t)row * stride);
+      }
+    }
+  };
 
   const float c = a.scale_log2;
   float m = -INFINITY;  // running max of head lo, in log2 units (same in all four lane groups)
@@ -119,48 +213,43 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(AttnArgs a) {
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) oacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Page-table entries of keys [kt, kt + 32): every lane loads (lanes 32..63 and
-  // keys past k1 re-read an in-range entry) so the load is unconditional.
-  auto load_entries = [&](int kt) -> int32_t { return pt_row[min(kt + (lane & 31), k1 - 1)]; };
-  // -1 marks a key past k1 or an entry outside the pool (reported)
-  auto check_entries = [&](int kt, int32_t e) -> int32_t {
-    const bool in_range = lane < kTileKeys && kt + lane < k1;
-    if (in_range && (e < 0 || (int64_t)e >= a.num_pool_rows)) {
-      raise_status(a.status, PKV_STATUS_BAD_PAGE_ROW);
-      e = -1;
-    }
-    return in_range ? e : -1;
-  };
-  u32x4 kr[8], vr[8];  // the rows of the tile in flight
-  auto issue = [&](int32_t e) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int64_t row = max(__shfl(e, 4 * u + (lane >> 4), 64), 0);  // missing keys read row 0
-      kr[u] = load16_stream(kbase + row * stride);
-      vr[u] = load16_stream(vbase + row * stride);
-    }
-  };
-
-  int32_t ent = check_entries(k0, load_entries(k0));
-  issue(ent);
+  // prologue: rows of tile f0 in flight, entries of tile f0 + 1 requested, q of f0's segment
+  Cursor cl = cc;  // the tile whose rows are in flight
+  Cursor ce = cc;  // the tile whose entries are in flight
+  int32_t ent = check_entries(ce, load_entries(ce));
+  issue(cl, ent);
   uint32_t valid_next = (uint32_t)__ballot(ent >= 0);  // bit k: key k of the tile has a row
-  int32_t ent_raw = (k0 + kTileKeys < k1) ? load_entries(k0 + kTileKeys) : -1;
-  for (int kt = k0; kt < k1; kt += kTileKeys) {
+  int32_t ent_raw = -1;
+  if (f0 + 1 < f1) {
+    advance(ce);
+    ent_raw = load_entries(ce);
+  }
+  bf16x8 qop[4], qnext[4];
+  load_q(cc, qop);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) qnext[kk] = qop[kk];
+
+  for (int32_t f = f0; f < f1; ++f) {
     const uint32_t valid = valid_next;
-    // this tile's rows -> the wavefront's row-major LDS tiles (a missing key's V is zeroed)
+    // this tile's rows -> the wavefront's row-major LDS tiles (a missing key's rows are zero)
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int key = 4 * u + (lane >> 4);
-      if (!((valid >> key) & 1u)) vr[u] = u32x4{0u, 0u, 0u, 0u};
       *reinterpret_cast<u32x4*>(&ktile[key * kKsPitch + lo * 8]) = kr[u];
       *reinterpret_cast<u32x4*>(&vtile[key * kVsPitch + lo * 8]) = vr[u];
     }
-    // the next tile's rows go out now and stay in flight while this one is computed
-    if (kt + kTileKeys < k1) {
-      ent = check_entries(kt + kTileKeys, ent_raw);
-      issue(ent);
+    // the next tile's rows (possibly of the next segment) go out now and stay
+    // in flight while this one is computed
+    if (f + 1 < f1) {
+      advance(cl);
+      ent = check_entries(cl, ent_raw);
+      issue(cl, ent);
       valid_next = (uint32_t)__ballot(ent >= 0);
-      if (kt + 2 * kTileKeys < k1) ent_raw = load_entries(kt + 2 * kTileKeys);
+      if (cl.kti == 0) load_q(cl, qnext);  // a new segment starts with the next tile
+      if (f + 2 < f1) {
+        advance(ce);
+        ent_raw = load_entries(ce);
+      }
     }
 
     // S^T (16 keys x 16 heads) per half tile; K operand: key 16 b + lo, dims (4 grp + kk) * 8
@@ -222,50 +311,81 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(AttnArgs a) {
       const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r1, r2, 0, 1, 2, 3, 4, 5, 6, 7));
       oacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop, oacc[mb], 0, 0, 0);
     }
-  }
 
-  // the four lane groups share the max: only the sums need reducing
-  float L = lsum;
-  L += shfl_xor(L, 16);
-  L += shfl_xor(L, 32);
-  if (lo >= G) return;
-  const int64_t hq = (int64_t)g * G + lo;
-  if (nsplit == 1) {  // the whole request in one item: normalise and write
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    uint16_t* orow = a.o + (tok * a.Hq + hq) * kHeadDim + 4 * grp;
+    // end of the segment or of the run: finish this piece
+    const bool seg_end = cc.kti == cc.n - 1;
+    if (seg_end || f + 1 == f1) {
+      // the four lane groups share the max: only the sums need reducing
+      float L = lsum;
+      L += shfl_xor(L, 16);
+      L += shfl_xor(L, 32);
+      const int64_t tok = token_of(cc);
+      const bool tok_ok = tok >= 0 && tok < a.T;
+      if (!tok_ok && lane == 0) raise_status(a.status, PKV_STATUS_TOKEN_COUNT);
+      const bool started_before = cc.seg < f0;
+      const int h = head_of(cc);
+      if (tok_ok && lo < G) {
+        const int64_t hq = (int64_t)h * G + lo;
+        if (!started_before && seg_end) {  // the whole segment: normalise and write
+          const float inv = L > 0.f ? 1.f / L : 0.f;
+          uint16_t* orow = a.o + (tok * a.Hq + hq) * kHeadDim + 4 * grp;
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
-      *reinterpret_cast<uint2*>(orow + 16 * mb) =
-          make_uint2(pack_bf16x2(oacc[mb][0] * inv, oacc[mb][1] * inv), pack_bf16x2(oacc[mb][2] * inv, oacc[mb][3] * inv));
-    return;
+          for (int mb = 0; mb < 8; ++mb)
+            *reinterpret_cast<uint2*>(orow + 16 * mb) = make_uint2(pack_bf16x2(oacc[mb][0] * inv, oacc[mb][1] * inv),
+                                                                  pack_bf16x2(oacc[mb][2] * inv, oacc[mb][3] * inv));
+        } else {  // a piece of a shared segment: publish (acc, max, sum)
+          const int64_t slot = (((int64_t)run * 2 + (started_before ? 0 : 1)) * HG + hw) * G + lo;
+          float* dst = a.ws_acc + slot * kHeadDim + 4 * grp;
+#pragma unroll
+          for (int mb = 0; mb < 8; ++mb)
+            *reinterpret_cast<float4*>(dst + 16 * mb) = make_float4(oacc[mb][0], oacc[mb][1], oacc[mb][2], oacc[mb][3]);
+          if (grp == 0) *reinterpret_cast<float2*>(a.ws_ml + slot * 2) = make_float2(m, L);
+        }
+      }
+      m = -INFINITY;
+      lsum = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) oacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) qop[kk] = qnext[kk];
+    }
+    if (f + 1 < f1) advance(cc);
   }
-  // several items: publish this item's (acc, max, sum) for the merge launch
-  float* dst = a.ws_acc + ((int64_t)item * a.Hq + hq) * kHeadDim + 4 * grp;
-#pragma unroll
-  for (int mb = 0; mb < 8; ++mb)
-    *reinterpret_cast<float4*>(dst + 16 * mb) = make_float4(oacc[mb][0], oacc[mb][1], oacc[mb][2], oacc[mb][3]);
-  if (grp == 0) *reinterpret_cast<float2*>(a.ws_ml + ((int64_t)item * a.Hq + hq) * 2) = make_float2(m, L);
 }
 
 // One workgroup per (request, pair of query heads), one thread per dimension:
-// a single pass over the request's items with a running max; the loads of an
-// item do not depend on the running state, so consecutive items overlap.
+// the pieces of a segment shared by runs w0 .. w1 are run w0's slot 1 and
+// slot 0 of runs w0 + 1 .. w1 (each at the KV head's wavefront); a single
+// pass with a running max combines them (their loads do not depend on the
+// running state, so they overlap).
 __global__ void __launch_bounds__(256) decode_merge_kernel(AttnArgs a) {
   const int i = blockIdx.x;
   const int hq = blockIdx.y * 2 + (threadIdx.x >> 7);
   const int d = threadIdx.x & 127;
   if (hq >= a.Hq) return;
-  const int32_t* req_items = reinterpret_cast<const int32_t*>(a.plan + a.layout.req_items_off);
-  const int j0 = req_items[i];
-  const int j1 = req_items[i + 1];
-  if (j1 - j0 <= 1) return;  // written by the first launch
+  const int32_t* header = reinterpret_cast<const int32_t*>(a.plan);
+  const int32_t per = header[1];
+  const int32_t* tptr = reinterpret_cast<const int32_t*>(a.plan + a.layout.dec_tiles_off);
+  const int32_t n = tptr[i + 1] - tptr[i];
+  if (n == 0) return;  // not a valid decode request
+  const int G = a.group;
+  const int g = hq / G;
+  const int gh = hq - g * G;
+  const int HG = decode_heads_per_group(a.Hkv);
+  const int gg = g / HG;
+  const int wv = g - gg * HG;
+  const int64_t seg = (int64_t)(a.Hkv / HG) * tptr[i] + (int64_t)gg * n;
+  const int64_t w0 = seg / per;
+  const int64_t w1 = (seg + n - 1) / per;
+  if (w0 == w1) return;  // written by the first launch
   const int64_t tok = a.qo_indptr[i];
   if (tok < 0 || tok >= a.T) return;
   float Mx = -INFINITY, den = 0.f, num = 0.f;
 #pragma unroll 4
-  for (int j = j0; j < j1; ++j) {
-    const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + ((int64_t)j * a.Hq + hq) * 2);
-    const float aj = a.ws_acc[((int64_t)j * a.Hq + hq) * kHeadDim + d];
+  for (int64_t w = w0; w <= w1; ++w) {
+    const int64_t slot = ((w * 2 + (w == w0 ? 1 : 0)) * HG + wv) * G + gh;
+    const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + slot * 2);
+    const float aj = a.ws_acc[slot * kHeadDim + d];
     const float Mn = fmaxf(Mx, ml.x);
     const float so = (Mx == -INFINITY) ? 0.f : fast_exp2(Mx - Mn);
     const float sn = (ml.x == -INFINITY) ? 0.f : fast_exp2(ml.x - Mn);
@@ -282,8 +402,7 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(AttnArgs a) {
 
 hipError_t launch_decode(const AttnArgs& a, hipStream_t s) {
   if (a.num_decode == 0) return hipSuccess;
-  const dim3 grid((unsigned)a.layout.cap_items, (unsigned)a.layout.kv_groups);
-  hipLaunchKernelGGL(decode_kernel, grid, dim3(64 * kWaves), 0, s, a);
+  hipLaunchKernelGGL(decode_kernel, dim3(kDecodeWaves / kWaves), dim3(64 * kWaves), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)a.num_decode, (unsigned)((a.Hq + 1) / 2)), dim3(256), 0, s, a);

@@ -62,7 +62,7 @@ struct AllocArgs {
 };
 
 struct MetaArgs {
-  int32_t B, num_decode, R, W, page_shift, group;
+  int32_t B, num_decode, R, W, page_shift, group, Hkv;
   int64_t T, num_pool_rows, num_alloc;
   const int32_t* table_idx;
   const int32_t* cached_len;
@@ -98,8 +98,8 @@ struct AttnArgs {
   uint16_t* o;
   const char* plan;
   PlanLayout layout;
-  float* ws_acc;           // [cap_items, Hq, d]
-  float* ws_ml;            // [cap_items, Hq, 2] (running max in log2 units, running sum)
+  float* ws_acc;           // [runs][2][HG][G][d] (runs x HG = kDecodeWaves): partial accumulators of split segments
+  float* ws_ml;            // [runs][2][HG][G][2]: their running max (log2 units) and sum
   int32_t* status;
 };
 

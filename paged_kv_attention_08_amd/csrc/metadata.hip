@@ -11,7 +11,9 @@
 // Two launches on the caller's stream:
 //   plan_kernel  (one workgroup): per-request validation, running totals
 //                (qo_indptr, kv_indptr, last_indices, alloc offsets), the
-//                decode split-K item list and the extend tile list;
+//                decode tile offsets and per-run share (the decode kernel
+//                splits the flat sequence of (request, group of KV heads, key
+//                tile) evenly over its runs) and the extend tile list;
 //   token_kernel (one thread per new token): finds its request by binary
 //                search over qo_indptr and writes page_table, out_loc and
 //                positions.
@@ -28,7 +30,7 @@ constexpr int kScanVals = 5;
 
 struct ReqInfo {
   bool valid;
-  int32_t ext, dl, new_pages, items, tiles;
+  int32_t ext, dl, new_pages, dtiles, tiles;
 };
 
 __device__ inline int32_t ceil_div_pow2(int32_t x, int32_t shift) {
@@ -80,45 +82,26 @@ __device__ inline void block_scan(int32_t (&v)[kScanVals], int32_t (&excl)[kScan
 
 __global__ void __launch_bounds__(kPlanThreads) plan_kernel(MetaArgs a) {
   __shared__ int32_t smem[kScanVals][kPlanWaves];
-  __shared__ long long red[kPlanWaves];
   const int tid = threadIdx.x;
   int32_t bits = 0;
   int32_t* header = (int32_t*)a.plan;
-  int4* items = (int4*)(a.plan + a.layout.items_off);
-  int32_t* req_items = (int32_t*)(a.plan + a.layout.req_items_off);
+  int32_t* dec_tile_ptr = (int32_t*)(a.plan + a.layout.dec_tiles_off);
   int2* tiles = (int2*)(a.plan + a.layout.tiles_off);
   int32_t* alloc_ptr = (int32_t*)(a.plan + a.layout.alloc_ptr_off);
   const int32_t s = a.page_shift;
   const int32_t tq = a.layout.tile_q;
 
-  // Pass 1: total keys of valid decode requests -> split size.
-  long long keys = 0;
-  for (int i = tid; i < a.num_decode; i += kPlanThreads) {
-    int32_t dummy = 0;
-    if (request_ok(a, i, &dummy)) keys += a.device_len[i];
-  }
-  for (int off = 32; off > 0; off >>= 1) keys += __shfl_xor(keys, off, 64);
-  if ((tid & 63) == 0) red[tid >> 6] = keys;
-  __syncthreads();
-  long long total_keys = 0;
-  for (int w = 0; w < kPlanWaves; ++w) total_keys += red[w];
-  // Split size: a multiple of 64 keys, at least 64, chosen so that the item
-  // count stays within cap_items = B + kDecodeTargetItems:
-  //   sum ceil(dl / chunk) <= total / chunk + B <= kDecodeTargetItems + B.
-  long long per = (total_keys + kDecodeTargetItems - 1) / kDecodeTargetItems;
-  int32_t chunk = (int32_t)align_up64(per > 64 ? per : 64, 64);
-
-  // Pass 2: running totals and work lists, 1024 requests at a time.
+  // Running totals and work lists, kPlanThreads requests at a time.
   int32_t carry[kScanVals] = {0, 0, 0, 0, 0};
   if (tid == 0) {
     a.qo_indptr[0] = 0;
     a.kv_indptr[0] = 0;
-    req_items[0] = 0;
+    dec_tile_ptr[0] = 0;
     alloc_ptr[0] = 0;
   }
   for (int base = 0; base < a.B; base += kPlanThreads) {
     const int i = base + tid;
-    ReqInfo ri = {false, 0, 0, 0, 0, 0};
+    ReqInfo ri = {false, 0, 0, 0, 0, 0};  // valid, ext, dl, new_pages, dtiles, tiles
     if (i < a.B) {
       const int32_t c = a.cached_len[i];
       const int32_t dl = a.device_len[i];
@@ -127,11 +110,11 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(MetaArgs a) {
       ri.dl = dl > 0 ? dl : 0;
       ri.new_pages = (c >= 0 && c <= dl) ? ceil_div_pow2(dl, s) - ceil_div_pow2(c, s) : 0;
       if (ri.valid) {
-        if (i < a.num_decode) ri.items = (dl + chunk - 1) / chunk;
+        if (i < a.num_decode) ri.dtiles = (dl + kDecodeTileKeys - 1) / kDecodeTileKeys;
         else ri.tiles = (ri.ext + tq - 1) / tq;
       }
     }
-    int32_t v[kScanVals] = {ri.ext, ri.dl, ri.new_pages, ri.items, ri.tiles};
+    int32_t v[kScanVals] = {ri.ext, ri.dl, ri.new_pages, ri.dtiles, ri.tiles};
     int32_t ex[kScanVals], tot[kScanVals];
     block_scan(v, ex, tot, smem);
     if (i < a.B) {
@@ -140,14 +123,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(MetaArgs a) {
       a.kv_indptr[i + 1] = carry[1] + ex[1] + ri.dl;
       a.last_indices[i] = qo_end - 1;
       alloc_ptr[i + 1] = carry[2] + ex[2] + ri.new_pages;
-      const int32_t ib = carry[3] + ex[3];
-      const int32_t cap_i = a.layout.cap_items;
-      req_items[i + 1] = min(ib + ri.items, cap_i);
-      for (int k = 0; k < ri.items && ib + k < cap_i; ++k) {
-        const int32_t k0 = k * chunk;
-        const int32_t k1 = min(ri.dl, k0 + chunk);
-        items[ib + k] = make_int4(i, k0, k1, ri.items);
-      }
+      dec_tile_ptr[i + 1] = carry[3] + ex[3] + ri.dtiles;
       const int32_t tb = carry[4] + ex[4];
       const int32_t cap_t = a.layout.cap_tiles;
       for (int k = 0; k < ri.tiles && tb + k < cap_t; ++k) {
@@ -159,11 +135,17 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(MetaArgs a) {
     for (int q = 0; q < kScanVals; ++q) carry[q] += tot[q];
   }
   if (tid == 0) {
-    header[0] = min(carry[3], a.layout.cap_items);
-    header[1] = chunk;
+    // the decode kernel's runs each take `per` consecutive tiles of the flat
+    // (request, KV-head group, key tile) order
+    const int32_t hg = decode_heads_per_group(a.Hkv);
+    const int64_t runs = kDecodeWaves / hg;
+    const int64_t total = (int64_t)(a.Hkv / hg) * carry[3];
+    const int64_t per = total > 0 ? (total + runs - 1) / runs : 1;
+    header[0] = (int32_t)total;
+    header[1] = (int32_t)per;
     header[2] = min(carry[4], a.layout.cap_tiles);
     header[3] = tq;
-    header[4] = a.layout.cap_items;
+    header[4] = (int32_t)((total + per - 1) / per);
     header[5] = a.layout.cap_tiles;
     if ((int64_t)carry[0] != a.T) bits |= PKV_STATUS_TOKEN_COUNT;
     if ((int64_t)carry[2] > a.num_alloc) bits |= PKV_STATUS_BAD_ALLOC;

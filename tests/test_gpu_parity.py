@@ -144,6 +144,14 @@ def _edge_workloads():
     cases.append(("group3", build_workload("group3", 45, [RequestSpec(70, 71), RequestSpec(12, 60)],
                                            num_qo_heads=6, num_kv_heads=2, head_dim=128, page_size=1,
                                            num_pool_rows=1024, num_decode=1)))
+    # KV head counts whose decode runs read 2 heads (6 KV heads) and 1 head (3 KV heads) at a time
+    cases.append(("kv6", build_workload("kv6", 56, [RequestSpec(700, 701), RequestSpec(64, 65), RequestSpec(2, 3),
+                                                    RequestSpec(10, 90)],
+                                        num_qo_heads=12, num_kv_heads=6, head_dim=128, page_size=1,
+                                        num_pool_rows=2048, num_decode=3)))
+    cases.append(("kv3", build_workload("kv3", 57, [RequestSpec(500, 501), RequestSpec(31, 32), RequestSpec(3, 40)],
+                                        num_qo_heads=12, num_kv_heads=3, head_dim=128, page_size=1,
+                                        num_pool_rows=2048, num_decode=2)))
     # other page sizes with partial pages on both ends
     for s in (2, 16, 32):
         cases.append((f"page{s}", build_workload(f"page{s}", 46 + s, [RequestSpec(5 * s + 3, 5 * s + 4),
