@@ -31,13 +31,14 @@ constexpr int kPlanHeaderInts = 16;
 //   [5] extend capacity
 // dec_tile_ptr   : int32 [B + 1]     first decode tile of each request (per KV head;
 //                                    0 tiles for extend and invalid requests)
-// extend tiles   : int2 [cap_tiles]  (request, first new-token offset)
+// extend tiles   : int2 [cap_tiles]  (request, first new-token offset), most keys first
+// tiles_raw      : int2 [cap_tiles]  the same, request by request (sort input)
 // alloc_ptr      : int32 [B + 1]     first alloc_rows entry of each request
 // The flat decode order is request-major, then group of HG KV heads, then key
 // tile: with Hg = Hkv / HG groups (HG = decode_heads_per_group(Hkv)), the
 // tiles of (request i, group gg) are Hg * dec_tile_ptr[i] + gg * n_i + [0, n_i).
 struct PlanLayout {
-  int64_t dec_tiles_off, tiles_off, alloc_ptr_off, total;
+  int64_t dec_tiles_off, tiles_off, tiles_raw_off, alloc_ptr_off, total;
   int32_t cap_tiles, tile_q;
 };
 
@@ -55,6 +56,7 @@ __host__ inline PlanLayout plan_layout(int32_t max_reqs, int64_t max_tokens, int
   int64_t off = kPlanHeaderInts * 4;
   L.dec_tiles_off = off;   off = align_up64(off + (int64_t)(max_reqs + 1) * 4, 16);
   L.tiles_off = off;       off += (int64_t)L.cap_tiles * 8;
+  L.tiles_raw_off = off;   off += (int64_t)L.cap_tiles * 8;
   L.alloc_ptr_off = off;   off = align_up64(off + (int64_t)(max_reqs + 1) * 4, 16);
   L.total = off;
   return L;

@@ -34,8 +34,10 @@
 //     keys, so the row max needs one cross-half shuffle;
 //   * causal masking is applied only on tiles that reach past the first
 //     row's position; prefix tiles run unmasked;
-//   * online softmax in fp32 (the max moves only when it grows by more than
-//     2^8, so the output accumulator is rarely rescaled);
+//   * online softmax in fp32 without a per-tile max pass: probabilities are
+//     taken against the running max and a lane's sum of them (computed anyway
+//     for the normaliser) detects growth past 2^64, after which the tile is
+//     redone against its true max (the first tile always is);
 //   * O^T += V^T P^T: the probabilities, rounded to bf16, are used as the B
 //     operand straight from the score accumulator registers (the key order of
 //     the contraction is permuted to match them); the V^T operand (8 keys of
@@ -126,7 +128,12 @@ __global__ void __launch_bounds__(64 * kWaves, 8 / kWaves) extend_kernel(AttnArg
 
   // loader: load u (0..kLoads-1) of lane l in wavefront w moves 16 bytes
   // (dims 8 (l % 16) ..) of key kWaveKeys w + 4 u + l / 16 of the tile.  Keys past kv_end
-  // re-read the last valid key's row (masked, V zeroed).
+  // re-read the last valid key's row: finite data, and such keys only occur in the
+  // last tile, which is always masked, so their probabilities are exactly 0.  Tiles
+  // past the end are gathered the same way: every tile issues the same loads, which
+  // lets the compiler wait only for the loads of the tile being stored (with
+  // conditional gathers it waited for the previous tile's loads as well, halving
+  // the prefetch distance).
   uint4 kpre[2][kLoads], vpre[2][kLoads];  // [register set][load]
   // page-table entries of the next tile to gather, one per load (16 lanes share one)
   int32_t ent[kLoads];
@@ -157,14 +164,6 @@ __global__ void __launch_bounds__(64 * kWaves, 8 / kWaves) extend_kernel(AttnArg
     }
     if (bad) raise_status(a.status, PKV_STATUS_BAD_PAGE_ROW);
   };
-  auto zero_tail = [&](int kt, auto set_tag) __attribute__((always_inline)) {
-    constexpr int SET = decltype(set_tag)::value;
-    if (kt + kKeyTile > kv_end) {
-#pragma unroll
-      for (int u = 0; u < kLoads; ++u)
-        if (kt + kWaveKeys * wave + 4 * u + (lane >> 4) >= kv_end) vpre[SET][u] = make_uint4(0, 0, 0, 0);
-    }
-  };
 
   f32x16 oacc[4];
 #pragma unroll
@@ -178,10 +177,10 @@ __global__ void __launch_bounds__(64 * kWaves, 8 / kWaves) extend_kernel(AttnArg
   // tiles whose keys all lie at or before the first row's position need no mask
   const int kt_mask = min(kv_end, ((min_pos + 1) / kKeyTile) * kKeyTile);
 
-  // tile kt from register set S into LDS stage S (a key past kv_end gets a zero V row)
+  // tile kt from register set S into LDS stage S
   auto store_tile = [&](int kt, auto set_tag) __attribute__((always_inline)) {
     constexpr int S = decltype(set_tag)::value;
-    zero_tail(kt, set_tag);
+    (void)kt;
 #pragma unroll
     for (int u = 0; u < kLoads; ++u) {
       const int key = kWaveKeys * wave + 4 * u + (lane >> 4);
@@ -197,10 +196,8 @@ __global__ void __launch_bounds__(64 * kWaves, 8 / kWaves) extend_kernel(AttnArg
     const bool MASK = kt >= kt_mask;  // uniform
     // the next tile goes to the other stage (last read before the previous
     // barrier); its register set then receives the tile three ahead
-    if (kt + kKeyTile < kv_end) {
-      store_tile(kt + kKeyTile, std::integral_constant<int, SET ^ 1>{});
-      if (kt + 3 * kKeyTile < kv_end) gather(kt + 3 * kKeyTile, std::integral_constant<int, SET ^ 1>{});
-    }
+    store_tile(kt + kKeyTile, std::integral_constant<int, SET ^ 1>{});
+    gather(kt + 3 * kKeyTile, std::integral_constant<int, SET ^ 1>{});
     const uint16_t* ks = ks_all[SET];
     const uint16_t* vs = vs_all[SET];
 
@@ -228,46 +225,60 @@ __global__ void __launch_bounds__(64 * kWaves, 8 / kWaves) extend_kernel(AttnArg
         for (int v = 0; v < 16; ++v)
           if (kt + 32 * mb + 8 * (v >> 2) + 4 * half + (v & 3) > pos) sacc[mb][v] = -INFINITY;
     }
-    float tmax = -INFINITY;
+    // Probabilities against the running max m without a max pass: p =
+    // exp2(s c - m), rounded to bf16 (the PV operand), and this lane's sum of
+    // its 32 of them.  A lane's sum bounds each of its p, so while every sum
+    // stays at or below 2^64 (and finite) nothing can overflow: fp32 and bf16
+    // keep their relative precision at any such magnitude, and the output is
+    // normalised by the same sum of bf16 values.  The first tile (m = -inf) and
+    // a tile whose scores grew by more than 64 (log2 units) since the last max
+    // take the slow path: the true tile max (both lane halves of a row), the
+    // rescale of the accumulator and sum, and the probabilities again.
+    uint32_t pk[2][8];  // bf16 pairs: block mb, words 4 kq + 0..3
+    float psum0, psum1;
+    auto make_p = [&](float nms) __attribute__((always_inline)) {
+      psum0 = 0.f;
+      psum1 = 0.f;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sacc[mb][v]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * csc;  // scale > 0 keeps the order
-    const bool upd = tmax > m + 8.f;
+        for (int w = 0; w < 8; ++w) {
+          const float p0 = fast_exp2(__builtin_fmaf(sacc[mb][2 * w], csc, nms));
+          const float p1 = fast_exp2(__builtin_fmaf(sacc[mb][2 * w + 1], csc, nms));
+          pk[mb][w] = pack_bf16x2(p0, p1);
+          if (w & 1) psum1 = dot2_bf16(pk[mb][w], psum1);
+          else psum0 = dot2_bf16(pk[mb][w], psum0);
+        }
+    };
     float alpha = 1.f;
-    if (upd) {
-      alpha = fast_exp2(m - tmax);
-      m = tmax;
+    bool slow = __ballot(m == -INFINITY) != 0;
+    if (!slow) {
+      make_p(-m);
+      slow = __ballot(!(psum0 + psum1 <= 0x1p64f)) != 0;
     }
-    if (__ballot(upd) != 0) {
+    if (slow) {
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sacc[mb][v]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * csc;  // scale > 0 keeps the order
+      const float mn = fmaxf(m, tmax);
+      alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mn);
+      m = mn;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) oacc[nb][v] *= alpha;
+      make_p(m == -INFINITY ? 0.f : -m);
     }
-    const float nms = (m == -INFINITY) ? 0.f : -m;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) sacc[mb][v] = fast_exp2(__builtin_fmaf(sacc[mb][v], csc, nms));
-    float psum0 = 0.f, psum1 = 0.f;
 
     // O^T += V^T P^T, 16 keys per MFMA
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int kq = 0; kq < 2; ++kq) {
-        uint4 pw;
-        pw.x = pack_bf16x2(sacc[mb][8 * kq + 0], sacc[mb][8 * kq + 1]);
-        pw.y = pack_bf16x2(sacc[mb][8 * kq + 2], sacc[mb][8 * kq + 3]);
-        pw.z = pack_bf16x2(sacc[mb][8 * kq + 4], sacc[mb][8 * kq + 5]);
-        pw.w = pack_bf16x2(sacc[mb][8 * kq + 6], sacc[mb][8 * kq + 7]);
-        psum0 = dot2_bf16(pw.x, psum0);
-        psum1 = dot2_bf16(pw.y, psum1);
-        psum0 = dot2_bf16(pw.z, psum0);
-        psum1 = dot2_bf16(pw.w, psum1);
-        const bf16x8 pop = as_bf16x8(pw);
+        const bf16x8 pop = as_bf16x8(make_uint4(pk[mb][4 * kq], pk[mb][4 * kq + 1], pk[mb][4 * kq + 2], pk[mb][4 * kq + 3]));
         // V^T operand: slots 0..3 are keys key0 + 0..3, slots 4..7 keys key0 + 8..11
         const int key0 = mb * 32 + 16 * kq + 4 * half;
         const int j16 = lane & 15;
@@ -286,17 +297,22 @@ __global__ void __launch_bounds__(64 * kWaves, 8 / kWaves) extend_kernel(AttnArg
 
   load_entries(0);
   gather(0, std::integral_constant<int, 0>{});
-  if (kKeyTile < kv_end) gather(kKeyTile, std::integral_constant<int, 1>{});
+  gather(kKeyTile, std::integral_constant<int, 1>{});
   store_tile(0, std::integral_constant<int, 0>{});
-  if (2 * kKeyTile < kv_end) gather(2 * kKeyTile, std::integral_constant<int, 0>{});
+  gather(2 * kKeyTile, std::integral_constant<int, 0>{});
   __syncthreads();
-  for (int kt = 0; kt < kv_end; kt += 2 * kKeyTile) {
+  // both tiles of a pair always run, so every path into a tile has the same
+  // loads in flight (an odd last tile runs after the loop)
+  int kt = 0;
+  for (; kt + kKeyTile < kv_end; kt += 2 * kKeyTile) {
     key_tile(kt, std::integral_constant<int, 0>{});
     __syncthreads();
-    if (kt + kKeyTile < kv_end) {
-      key_tile(kt + kKeyTile, std::integral_constant<int, 1>{});
-      __syncthreads();
-    }
+    key_tile(kt + kKeyTile, std::integral_constant<int, 1>{});
+    __syncthreads();
+  }
+  if (kt < kv_end) {
+    key_tile(kt, std::integral_constant<int, 0>{});
+    __syncthreads();
   }
 
   const float L = lsum + __shfl_xor(lsum, 32, 64);

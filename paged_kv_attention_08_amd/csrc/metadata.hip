@@ -13,7 +13,9 @@
 //                (qo_indptr, kv_indptr, last_indices, alloc offsets), the
 //                decode tile offsets and per-run share (the decode kernel
 //                splits the flat sequence of (request, group of KV heads, key
-//                tile) evenly over its runs) and the extend tile list;
+//                tile) evenly over its runs) and the extend tile list,
+//                ordered by key count, most first (so the last workgroups to
+//                start are the shortest and the CUs finish together);
 //   token_kernel (one thread per new token): finds its request by binary
 //                search over qo_indptr and writes page_table, out_loc and
 //                positions.
@@ -27,6 +29,8 @@ namespace {
 constexpr int kPlanThreads = 256;
 constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kScanVals = 5;
+constexpr int kSortBuckets = 1024;  // extend tiles sorted by key count in steps of 64 keys (capped)
+static_assert(kSortBuckets % kPlanThreads == 0, "whole buckets per thread");
 
 struct ReqInfo {
   bool valid;
@@ -87,6 +91,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(MetaArgs a) {
   int32_t* header = (int32_t*)a.plan;
   int32_t* dec_tile_ptr = (int32_t*)(a.plan + a.layout.dec_tiles_off);
   int2* tiles = (int2*)(a.plan + a.layout.tiles_off);
+  int2* tiles_raw = (int2*)(a.plan + a.layout.tiles_raw_off);
   int32_t* alloc_ptr = (int32_t*)(a.plan + a.layout.alloc_ptr_off);
   const int32_t s = a.page_shift;
   const int32_t tq = a.layout.tile_q;
@@ -128,7 +133,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(MetaArgs a) {
       const int32_t cap_t = a.layout.cap_tiles;
       for (int k = 0; k < ri.tiles && tb + k < cap_t; ++k) {
         // longest tiles (largest token offset, most keys) first
-        tiles[tb + k] = make_int2(i, (ri.tiles - 1 - k) * tq);
+        tiles_raw[tb + k] = make_int2(i, (ri.tiles - 1 - k) * tq);
       }
     }
 #pragma unroll
@@ -151,6 +156,48 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(MetaArgs a) {
     if ((int64_t)carry[2] > a.num_alloc) bits |= PKV_STATUS_BAD_ALLOC;
   }
   if (bits) raise_status(a.status, bits);
+
+  // Extend tiles by key count, most first: a counting sort over kSortBuckets
+  // buckets of 64 keys.  Workgroups start in list order, so the longest run
+  // first and the shortest fill the last gaps (longest-processing-time
+  // order).  The order inside a bucket is whatever the LDS atomics give;
+  // every tile's result is independent of it.
+  __shared__ int32_t bucket[kSortBuckets];
+  const int32_t n_t = min(carry[4], a.layout.cap_tiles);
+  auto tile_bucket = [&](int2 t) -> int {
+    const int32_t ci = a.cached_len[t.x];
+    const int32_t di = a.device_len[t.x];
+    const int32_t kv_end = min(di, ci + t.y + tq);
+    return kSortBuckets - 1 - min(max(kv_end, 0) >> 6, kSortBuckets - 1);
+  };
+  for (int b = tid; b < kSortBuckets; b += kPlanThreads) bucket[b] = 0;
+  __syncthreads();  // also orders the tiles_raw writes above before the reads below
+  for (int t = tid; t < n_t; t += kPlanThreads) atomicAdd(&bucket[tile_bucket(tiles_raw[t])], 1);
+  __syncthreads();
+  {
+    constexpr int kPer = kSortBuckets / kPlanThreads;
+    int32_t cnt[kPer];
+    int32_t mine = 0;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      cnt[q] = bucket[tid * kPer + q];
+      mine += cnt[q];
+    }
+    int32_t v[kScanVals] = {mine, 0, 0, 0, 0};
+    int32_t ex[kScanVals], tot[kScanVals];
+    block_scan(v, ex, tot, smem);
+    int32_t run = ex[0];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      bucket[tid * kPer + q] = run;  // first position of the bucket
+      run += cnt[q];
+    }
+  }
+  __syncthreads();
+  for (int t = tid; t < n_t; t += kPlanThreads) {
+    const int2 tt = tiles_raw[t];
+    tiles[atomicAdd(&bucket[tile_bucket(tt)], 1)] = tt;
+  }
 }
 
 __global__ void __launch_bounds__(256) token_kernel(MetaArgs a) {
