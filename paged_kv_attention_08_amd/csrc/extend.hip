@@ -109,7 +109,9 @@ __global__ void __launch_bounds__(64 * kWaves, 8 / kWaves) extend_kernel(AttnArg
   const int gh = row - tq * G;
   const int64_t token = tokbase + t0 + tq;
   const bool row_valid = (tq < n_tok) && token >= 0 && token < a.T;
-  const int pos = row_valid ? c + t0 + tq : -1;
+  // a row past the tile's tokens sees every key (its q is zero and it is
+  // never written), so its running max is finite after the first tile
+  const int pos = row_valid ? c + t0 + tq : 0x7fffffff;
   const int h = g * G + gh;
 
   bf16x8 qop[8];
