@@ -152,6 +152,11 @@ def _edge_workloads():
     cases.append(("kv3", build_workload("kv3", 57, [RequestSpec(500, 501), RequestSpec(31, 32), RequestSpec(3, 40)],
                                         num_qo_heads=12, num_kv_heads=3, head_dim=128, page_size=1,
                                         num_pool_rows=2048, num_decode=2)))
+    # a pool of 4 GiB per K and V: extend gathers take 64-bit row offsets
+    cases.append(("wide_pool", build_workload("wide_pool", 58, [RequestSpec(900, 901), RequestSpec(300, 470),
+                                                                RequestSpec(0, 129)],
+                                              num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=1,
+                                              num_pool_rows=(1 << 21) + 64, num_decode=1)))
     # other page sizes with partial pages on both ends
     for s in (2, 16, 32):
         cases.append((f"page{s}", build_workload(f"page{s}", 46 + s, [RequestSpec(5 * s + 3, 5 * s + 4),
