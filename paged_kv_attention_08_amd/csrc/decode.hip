@@ -86,6 +86,18 @@ __device__ inline u32x4 load16_stream(const uint16_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// Uniform reads of data no launch of this call writes (plan, lengths, token
+// offsets, table rows) go through the constant address space, so they become
+// scalar loads with their own counter: as vector loads, every wait for them
+// also waited for the 16 row loads just issued for the next tile.  (Measured
+// neutral at the serving, long-context and page-64 batches: the other
+// wavefront of each SIMD covered that stall; the loop now keeps a tile of rows
+// in flight per wavefront as intended.)
+template <typename T>
+__device__ inline T ldu(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)(p);
+}
+
 // Position in the flat decode order (uniform across the wavefront).
 struct Cursor {
   int32_t i;    // request
@@ -105,8 +117,8 @@ __global__ void __launch_bounds__(64 * kWaves, 1) decode_kernel(AttnArgs a) {
   const int lo = lane & 15;
   const int grp = lane >> 4;
   const int32_t* header = reinterpret_cast<const int32_t*>(a.plan);
-  const int32_t total = header[0];
-  const int32_t per = header[1];
+  const int32_t total = ldu(header);
+  const int32_t per = ldu(header + 1);
   const int Hkv = a.Hkv;
   const int HG = decode_heads_per_group(Hkv);
   const int Hg = Hkv / HG;
@@ -125,16 +137,17 @@ __global__ void __launch_bounds__(64 * kWaves, 1) decode_kernel(AttnArgs a) {
     int lo_i = 0, hi_i = a.num_decode;  // tptr[num_decode] * Hg = total > f0
     while (hi_i - lo_i > 1) {
       const int mid = (lo_i + hi_i) >> 1;
-      if ((int64_t)Hg * tptr[mid] <= f0) lo_i = mid;
+      if ((int64_t)Hg * ldu(tptr + mid) <= f0) lo_i = mid;
       else hi_i = mid;
     }
     cc.i = lo_i;
-    cc.n = tptr[lo_i + 1] - tptr[lo_i];
-    const int32_t local = f0 - Hg * tptr[lo_i];
+    const int32_t t_lo = ldu(tptr + lo_i);
+    cc.n = ldu(tptr + lo_i + 1) - t_lo;
+    const int32_t local = f0 - Hg * t_lo;
     cc.g = local / cc.n;
     cc.kti = local - cc.g * cc.n;
-    cc.seg = Hg * tptr[lo_i] + cc.g * cc.n;
-    cc.dl = a.device_len[lo_i];
+    cc.seg = Hg * t_lo + cc.g * cc.n;
+    cc.dl = ldu(a.device_len + lo_i);
   }
   // next tile of the flat order (only called while one exists in the run)
   auto advance = [&](Cursor& c) __attribute__((always_inline)) {
@@ -145,13 +158,13 @@ __global__ void __launch_bounds__(64 * kWaves, 1) decode_kernel(AttnArgs a) {
         c.g = 0;
         do {
           ++c.i;
-        } while (tptr[c.i + 1] == tptr[c.i]);  // requests without decode tiles
-        c.n = tptr[c.i + 1] - tptr[c.i];
-        c.dl = a.device_len[c.i];
+        } while (ldu(tptr + c.i + 1) == ldu(tptr + c.i));  // requests without decode tiles
+        c.n = ldu(tptr + c.i + 1) - ldu(tptr + c.i);
+        c.dl = ldu(a.device_len + c.i);
       }
     }
   };
-  auto token_of = [&](const Cursor& c) -> int64_t { return a.qo_indptr[c.i]; };
+  auto token_of = [&](const Cursor& c) -> int64_t { return ldu(a.qo_indptr + c.i); };
   // this wavefront's KV head in c's group
   auto head_of = [&](const Cursor& c) -> int { return c.g * HG + hw; };
 
@@ -175,7 +188,7 @@ __global__ void __launch_bounds__(64 * kWaves, 1) decode_kernel(AttnArgs a) {
   // Page-table entries of the 32 keys of c's tile: every lane loads (lanes
   // 32..63 and keys past device_len re-read an in-range entry).
   auto load_entries = [&](const Cursor& c) -> int32_t {
-    const int32_t* pt_row = a.page_table + (int64_t)a.table_idx[c.i] * a.W;
+    const int32_t* pt_row = a.page_table + (int64_t)ldu(a.table_idx + c.i) * a.W;
     return pt_row[min(c.kti * kTileKeys + (lane & 31), c.dl - 1)];
   };
   // -1 marks a key past device_len or an entry outside the pool (reported)
