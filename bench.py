@@ -223,7 +223,7 @@ def main(argv=None):
     ap.add_argument("--flush", action="store_true", help="flush L2/MALL before every step (outside the events)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--layout", choices=["layer_first", "page_first"], default="layer_first",
+    ap.add_argument("--layout", choices=["layer_first", "page_first", "row_interleaved"], default="layer_first",
                     help="physical order of a multi-layer KV cache whose layer 0 the step runs on")
     ap.add_argument("--layers", type=int, default=1, help="layers in that cache (1: a plain one-layer pool)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -262,7 +262,8 @@ def main(argv=None):
     pool = None
     if args.layers > 1 or args.layout != "layer_first":
         import paged_kv_attention_08_amd as pkv
-        layout = pkv.KVCacheTensors.PAGE_FIRST if args.layout == "page_first" else pkv.KVCacheTensors.LAYER_FIRST
+        layout = {"layer_first": pkv.KVCacheTensors.LAYER_FIRST, "page_first": pkv.KVCacheTensors.PAGE_FIRST,
+                  "row_interleaved": pkv.KVCacheTensors.ROW_INTERLEAVED}[args.layout]
         cache = pkv.KVCacheTensors(args.layers, w.num_pool_rows, w.num_kv_heads, w.head_dim, w.page_size, layout)
         pool = cache.layer(0)
     ds = DeviceStep(w, pool=pool)

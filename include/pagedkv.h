@@ -217,16 +217,22 @@ int paged_extend_attn(const pkv_kv_pool* pool, const pkv_page_table* page_table,
 /* ---- all layers' KV cache in one buffer ------------------------------------ */
 
 /* The engine's KV cache (deep dive 6.2, MHAKVCache): one bf16 buffer holding K
- * (index 0) and V (index 1) of every layer.  Two physical orders:
+ * (index 0) and V (index 1) of every layer.  Three physical orders:
  *   PKV_LAYOUT_LAYER_FIRST : [2][num_layers][num_rows][Hkv][head_dim]
  *                            (a layer's rows are contiguous)
  *   PKV_LAYOUT_PAGE_FIRST  : [2][num_rows][num_layers][Hkv][head_dim]
  *                            (a row's layers are contiguous; the pages' permuted
  *                            view has the same logical shape, but a layer's rows
  *                            are num_layers * Hkv * head_dim elements apart)
+ *   PKV_LAYOUT_ROW_INTERLEAVED : [num_rows][num_layers][2][Hkv][head_dim]
+ *                            (a row's K and V of every layer are contiguous,
+ *                            so a gathered row's K and V lie on one memory
+ *                            page: half the address translations of separate
+ *                            K and V buffers when rows are scattered)
  * Every call works on one layer's pkv_kv_pool, obtained with pkv_kv_cache_layer. */
-#define PKV_LAYOUT_LAYER_FIRST 0
-#define PKV_LAYOUT_PAGE_FIRST  1
+#define PKV_LAYOUT_LAYER_FIRST     0
+#define PKV_LAYOUT_PAGE_FIRST      1
+#define PKV_LAYOUT_ROW_INTERLEAVED 2
 
 typedef struct pkv_kv_cache {
   void* data;              /* device, 16-byte aligned */

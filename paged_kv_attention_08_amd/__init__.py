@@ -93,16 +93,19 @@ class KVPoolTensors:
 
 class KVCacheTensors:
     """All layers' K and V in one bf16 buffer, in the engine's layer-first
-    ([2, L, N, Hkv, d]) or page-first ([2, N, L, Hkv, d]) physical order;
-    layer(i) is that layer's pool for the four calls."""
+    ([2, L, N, Hkv, d]), page-first ([2, N, L, Hkv, d]) or row-interleaved
+    ([N, L, 2, Hkv, d]: a row's K and V side by side) physical order; layer(i)
+    is that layer's pool for the four calls."""
 
     LAYER_FIRST = _lib.PKV_LAYOUT_LAYER_FIRST
     PAGE_FIRST = _lib.PKV_LAYOUT_PAGE_FIRST
+    ROW_INTERLEAVED = _lib.PKV_LAYOUT_ROW_INTERLEAVED
 
     def __init__(self, num_layers: int, num_rows: int, num_kv_heads: int, head_dim: int = 128, page_size: int = 1,
                  layout: int = _lib.PKV_LAYOUT_LAYER_FIRST, device="cuda"):
-        shape = ((2, num_layers, num_rows, num_kv_heads, head_dim) if layout == self.LAYER_FIRST
-                 else (2, num_rows, num_layers, num_kv_heads, head_dim))
+        shape = {self.LAYER_FIRST: (2, num_layers, num_rows, num_kv_heads, head_dim),
+                 self.PAGE_FIRST: (2, num_rows, num_layers, num_kv_heads, head_dim),
+                 self.ROW_INTERLEAVED: (num_rows, num_layers, 2, num_kv_heads, head_dim)}[layout]
         self.data = torch.zeros(shape, dtype=torch.bfloat16, device=device)
         self.num_layers, self.num_rows, self.layout = num_layers, num_rows, layout
         self.num_kv_heads, self.head_dim, self.page_size = num_kv_heads, head_dim, page_size
@@ -121,8 +124,10 @@ class KVCacheTensors:
         """Views of one layer's K and V rows; their struct() equals layer_struct()."""
         if self.layout == self.LAYER_FIRST:
             k, v = self.data[0, layer_id], self.data[1, layer_id]
-        else:
+        elif self.layout == self.PAGE_FIRST:
             k, v = self.data[0, :, layer_id], self.data[1, :, layer_id]
+        else:
+            k, v = self.data[:, layer_id, 0], self.data[:, layer_id, 1]
         pool = KVPoolTensors(k, v, self.page_size)
         want, got = self.layer_struct(layer_id), pool.struct()
         if (want.k, want.v, want.row_stride) != (got.k, got.v, got.row_stride):

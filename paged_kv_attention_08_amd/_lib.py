@@ -49,6 +49,7 @@ class AttnMetadata(ctypes.Structure):
 
 PKV_LAYOUT_LAYER_FIRST = 0
 PKV_LAYOUT_PAGE_FIRST = 1
+PKV_LAYOUT_ROW_INTERLEAVED = 2
 
 
 class KVCache(ctypes.Structure):

@@ -290,7 +290,9 @@ int pkv_free_pages(const pkv_free_list* free_list, const int32_t* rows, int32_t 
 int pkv_kv_cache_layer(const pkv_kv_cache* cache, int32_t layer_id, pkv_kv_pool* pool) {
   if (!cache || !pool || !cache->data || !aligned16(cache->data) || cache->reserved != 0) return PKV_ERR_INVALID_ARGUMENT;
   if (cache->num_layers <= 0 || layer_id < 0 || layer_id >= cache->num_layers) return PKV_ERR_INVALID_ARGUMENT;
-  if (cache->layout != PKV_LAYOUT_LAYER_FIRST && cache->layout != PKV_LAYOUT_PAGE_FIRST) return PKV_ERR_INVALID_ARGUMENT;
+  if (cache->layout != PKV_LAYOUT_LAYER_FIRST && cache->layout != PKV_LAYOUT_PAGE_FIRST &&
+      cache->layout != PKV_LAYOUT_ROW_INTERLEAVED)
+    return PKV_ERR_INVALID_ARGUMENT;
   if (cache->head_dim != kHeadDim) return PKV_ERR_UNSUPPORTED;
   if (cache->num_kv_heads <= 0 || cache->num_rows <= 0) return PKV_ERR_INVALID_ARGUMENT;
   const int64_t row = (int64_t)cache->num_kv_heads * cache->head_dim;  // elements of one layer's row
@@ -300,10 +302,14 @@ int pkv_kv_cache_layer(const pkv_kv_cache* cache, int32_t layer_id, pkv_kv_pool*
     k_off = (int64_t)layer_id * N * row;
     v_off = (L + layer_id) * N * row;
     stride = row;
-  } else {
+  } else if (cache->layout == PKV_LAYOUT_PAGE_FIRST) {
     k_off = (int64_t)layer_id * row;
     v_off = N * L * row + (int64_t)layer_id * row;
     stride = L * row;
+  } else {
+    k_off = (int64_t)layer_id * 2 * row;
+    v_off = k_off + row;
+    stride = L * 2 * row;
   }
   pkv_kv_pool p;
   p.k = static_cast<uint16_t*>(cache->data) + k_off;

@@ -264,7 +264,8 @@ def test_page_allocator_rejects(lib):
     assert lib.pkv_free_list_reset(B(fl), -1, None) == _lib.PKV_ERR_INVALID_ARGUMENT
 
 
-@pytest.mark.parametrize("layout", [_lib.PKV_LAYOUT_LAYER_FIRST, _lib.PKV_LAYOUT_PAGE_FIRST])
+@pytest.mark.parametrize("layout", [_lib.PKV_LAYOUT_LAYER_FIRST, _lib.PKV_LAYOUT_PAGE_FIRST,
+                                    _lib.PKV_LAYOUT_ROW_INTERLEAVED])
 def test_kv_cache_layer_pointers(lib, layout):
     """Host-only pointer arithmetic of the multi-layer cache (nothing launched)."""
     base, L, N, hkv, d = 1 << 20, 3, 4096, 8, 128
@@ -275,14 +276,16 @@ def test_kv_cache_layer_pointers(lib, layout):
         assert lib.pkv_kv_cache_layer(B(c), layer, B(p)) == _lib.PKV_OK
         if layout == _lib.PKV_LAYOUT_LAYER_FIRST:
             k_elem, v_elem, stride = layer * N * row, (L + layer) * N * row, row
-        else:
+        elif layout == _lib.PKV_LAYOUT_PAGE_FIRST:
             k_elem, v_elem, stride = layer * row, N * L * row + layer * row, L * row
+        else:
+            k_elem, v_elem, stride = 2 * layer * row, 2 * layer * row + row, 2 * L * row
         assert (p.k, p.v, p.row_stride) == (base + 2 * k_elem, base + 2 * v_elem, stride)
         assert (p.num_rows, p.page_size, p.num_kv_heads, p.head_dim) == (N, 16, hkv, d)
     p = _lib.KVPool()
     assert lib.pkv_kv_cache_layer(B(c), L, B(p)) == _lib.PKV_ERR_INVALID_ARGUMENT
     assert lib.pkv_kv_cache_layer(B(c), -1, B(p)) == _lib.PKV_ERR_INVALID_ARGUMENT
-    assert lib.pkv_kv_cache_layer(B(_lib.KVCache(base, N, L, 2, 16, hkv, d, 0)), 0, B(p)) == \
+    assert lib.pkv_kv_cache_layer(B(_lib.KVCache(base, N, L, 3, 16, hkv, d, 0)), 0, B(p)) == \
         _lib.PKV_ERR_INVALID_ARGUMENT
     assert lib.pkv_kv_cache_layer(B(_lib.KVCache(base, N, L, layout, 16, hkv, 64, 0)), 0, B(p)) == \
         _lib.PKV_ERR_UNSUPPORTED

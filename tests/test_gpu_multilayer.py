@@ -1,5 +1,5 @@
 """GPU parity of the step on one layer of a multi-layer KV cache (deep dive
-6.2: one buffer for all layers, layer-first or page-first), through the C
+6.2: one buffer for all layers, layer-first, page-first or row-interleaved), through the C
 ABI: each layer holds different values on the same pages; running every
 layer's store and attention gives each layer the oracle's result for its own
 values, and never touches another layer's rows."""
@@ -28,8 +28,9 @@ def layer_workload(w, layer):
                                q=np.roll(w.q, layer, axis=0))
 
 
-@pytest.mark.parametrize("layout", [pkv.KVCacheTensors.LAYER_FIRST, pkv.KVCacheTensors.PAGE_FIRST],
-                         ids=["layer_first", "page_first"])
+@pytest.mark.parametrize("layout", [pkv.KVCacheTensors.LAYER_FIRST, pkv.KVCacheTensors.PAGE_FIRST,
+                                    pkv.KVCacheTensors.ROW_INTERLEAVED],
+                         ids=["layer_first", "page_first", "row_interleaved"])
 @pytest.mark.parametrize("cfg", [2, 5])
 def test_each_layer_matches_oracle(layout, cfg):
     w = configs.small(cfg)
