@@ -226,6 +226,9 @@ def main(argv=None):
     ap.add_argument("--layout", choices=["layer_first", "page_first", "row_interleaved"], default="layer_first",
                     help="physical order of a multi-layer KV cache whose layer 0 the step runs on")
     ap.add_argument("--layers", type=int, default=1, help="layers in that cache (1: a plain one-layer pool)")
+    ap.add_argument("--page-order", choices=["random", "sequential"], default="random",
+                    help="physical page order of the workload: a random order of the free pages (default, rows "
+                         "scattered over the pool) or allocation order (a fresh pool's free list)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (torch copy_) 5 times: the known-size reference "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
@@ -257,7 +260,7 @@ def main(argv=None):
                           "launches": 5}), flush=True)
         return 0
     log(f"generating config {args.config}")
-    w = configs.FULL[args.config]()
+    w = configs.FULL[args.config](page_order=args.page_order)
     log(w.summary())
     pool = None
     if args.layers > 1 or args.layout != "layer_first":
@@ -356,7 +359,7 @@ def main(argv=None):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.config], "config_index": args.config,
                    "global_batch": w.num_reqs, "new_tokens": w.num_tokens, "parallelism": "single GPU",
-                   "l2_mall_flush_between_steps": bool(args.flush),
+                   "l2_mall_flush_between_steps": bool(args.flush), "page_order": args.page_order,
                    "kv_cache": f"{args.layers} layer(s), {args.layout}, step on layer 0"},
         "breakdown_ms": {"metadata": round(float(mean_ms[0]), 4), "kv_store": round(float(mean_ms[1]), 4),
                          "decode": round(float(mean_ms[2]), 4), "extend": round(float(mean_ms[3]), 4),

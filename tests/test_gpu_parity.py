@@ -164,6 +164,12 @@ def _edge_workloads():
                                                                       RequestSpec(0, 1, padding=True)],
                                                  num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=s,
                                                  num_pool_rows=64 * s, num_decode=1)))
+    # pages in allocation order (a fresh pool's free list) instead of a random order
+    cases.append(("seq_pages", configs.extend_radix(seed=59, nreq=3, prefix=96, tail_hi=70, chunk=83,
+                                                    num_pool_rows=1 << 13, page_order="sequential")))
+    cases.append(("seq_pages64", configs.mixed_page64(seed=61, ndec=6, dec_lo=1, dec_hi=300, next_=3, pre_hi=200,
+                                                      new_tokens=150, num_pool_rows=64 * 64,
+                                                      page_order="sequential")))
     # one long decode request spread over many splits, width exactly its length rounded to 32
     cases.append(("long_single", build_workload("long_single", 50, [RequestSpec(20000, 20001)],
                                                 num_qo_heads=64, num_kv_heads=8, head_dim=128, page_size=1,

@@ -56,3 +56,32 @@ def test_shared_prefix_rows_are_shared():
     rows = [w.page_table[w.table_idx[i], :96] for i in range(w.num_reqs)]
     for r in rows[1:]:
         assert np.array_equal(r, rows[0])
+
+
+@pytest.mark.parametrize("page_size", [1, 64])
+def test_sequential_page_order(page_size):
+    """Allocation-order pages: the same batch as the random order, with the pages
+    handed out 1, 2, 3, ... (prefix first, then each request's cached and new pages)."""
+    if page_size == 1:
+        kw = dict(nreq=3, prefix=96, tail_hi=70, chunk=83, num_pool_rows=1 << 13)
+        seq = configs.extend_radix(page_order="sequential", **kw)
+        rnd = configs.extend_radix(**kw)
+    else:
+        kw = dict(ndec=6, dec_lo=1, dec_hi=300, next_=3, pre_hi=200, new_tokens=150, num_pool_rows=64 * 64)
+        seq = configs.mixed_page64(page_order="sequential", **kw)
+        rnd = configs.mixed_page64(**kw)
+    assert np.array_equal(seq.cached_len, rnd.cached_len) and np.array_equal(seq.device_len, rnd.device_len)
+    assert np.array_equal(seq.q, rnd.q)
+    s = page_size
+    pages = []
+    for i in range(seq.num_reqs):
+        if seq.is_padding[i]:
+            continue
+        r, c = seq.table_idx[i], int(seq.cached_len[i])
+        pages.append(seq.page_table[r, :c:s].astype(np.int64) // s)
+    allp = np.concatenate(pages + [seq.alloc_rows[seq.alloc_rows != 0].astype(np.int64) // s])
+    uniq = np.unique(allp)
+    assert np.array_equal(uniq, np.arange(1, uniq.size + 1))   # pages 1..n, none skipped
+    with pytest.raises(ValueError):
+        configs.extend_radix(page_order="sorted", **dict(nreq=2, prefix=32, tail_hi=8, chunk=8,
+                                                          num_pool_rows=1 << 10))

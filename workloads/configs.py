@@ -20,7 +20,8 @@ def _length_rng(seed: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed).spawn(1)[0]))
 
 
-def tiny_decode(seed: int = 1001, batch: int = 4, lo: int = 64, hi: int = 256, num_pool_rows: int = 4096) -> Workload:
+def tiny_decode(seed: int = 1001, batch: int = 4, lo: int = 64, hi: int = 256, num_pool_rows: int = 4096,
+                page_order: str = "random") -> Workload:
     """Single-layer decode, 16 query / 8 KV heads, page_size 1, pool of 4096 rows.
 
     Context length L ~ U{lo..hi}; the step stores one new row per request, so
@@ -31,10 +32,11 @@ def tiny_decode(seed: int = 1001, batch: int = 4, lo: int = 64, hi: int = 256, n
     reqs = [RequestSpec(int(l), int(l) + 1) for l in L]
     return build_workload("tiny_decode", seed, reqs, num_qo_heads=16, num_kv_heads=8, head_dim=128,
                           page_size=1, num_pool_rows=num_pool_rows, num_decode=batch,
-                          width=((hi + 1 + 31) // 32) * 32)
+                          width=((hi + 1 + 31) // 32) * 32, page_order=page_order)
 
 
 def serving_decode(seed: int = 1002, real: int = 200, padded_to: int = 256, lo: int = 512, hi: int = 4096,
+                   page_order: str = "random",
                    num_pool_rows: int = 1 << 21, num_qo_heads: int = 32) -> Workload:
     """Llama-3-8B-like decode: 200 real requests padded with dummies to 256."""
     rng = _length_rng(seed)
@@ -43,11 +45,11 @@ def serving_decode(seed: int = 1002, real: int = 200, padded_to: int = 256, lo: 
     reqs += [RequestSpec(0, 1, padding=True) for _ in range(padded_to - real)]
     return build_workload("serving_decode", seed, reqs, num_qo_heads=num_qo_heads, num_kv_heads=8, head_dim=128,
                           page_size=1, num_pool_rows=num_pool_rows, num_decode=padded_to,
-                          width=((hi + 1 + 31) // 32) * 32)
+                          width=((hi + 1 + 31) // 32) * 32, page_order=page_order)
 
 
 def extend_radix(seed: int = 1003, nreq: int = 8, prefix: int = 2048, tail_hi: int = 1024, chunk: int = 1024,
-                 num_pool_rows: int = 1 << 20) -> Workload:
+                 num_pool_rows: int = 1 << 20, page_order: str = "random") -> Workload:
     """Chunked prefill on a radix-shared prefix: every request's first `prefix`
     cached tokens are the same physical rows; private cached tail ~ U{0..tail_hi};
     `chunk` new tokens per request."""
@@ -56,14 +58,14 @@ def extend_radix(seed: int = 1003, nreq: int = 8, prefix: int = 2048, tail_hi: i
     reqs = [RequestSpec(prefix + int(t), prefix + int(t) + chunk, shared_prefix=prefix) for t in tails]
     return build_workload("extend_radix", seed, reqs, num_qo_heads=32, num_kv_heads=8, head_dim=128,
                           page_size=1, num_pool_rows=num_pool_rows, num_decode=0,
-                          width=((prefix + tail_hi + chunk + 31) // 32) * 32)
+                          width=((prefix + tail_hi + chunk + 31) // 32) * 32, page_order=page_order)
 
 
 LONG_DECODE_POOL_ROWS = 36_621_056   # 150.0e9 bytes of K+V at 8 KV heads x 128 x bf16
 
 
 def long_decode(seed: int = 1004, batch: int = 32, lo: int = 16384, hi: int = 32768,
-                num_pool_rows: int = LONG_DECODE_POOL_ROWS) -> Workload:
+                num_pool_rows: int = LONG_DECODE_POOL_ROWS, page_order: str = "random") -> Workload:
     """70B-like layer (64 query / 8 KV heads) decode over 16K-32K contexts in a
     ~150 GB pool; rows are scattered uniformly over the whole pool."""
     rng = _length_rng(seed)
@@ -71,12 +73,12 @@ def long_decode(seed: int = 1004, batch: int = 32, lo: int = 16384, hi: int = 32
     reqs = [RequestSpec(int(l), int(l) + 1) for l in L]
     return build_workload("long_decode", seed, reqs, num_qo_heads=64, num_kv_heads=8, head_dim=128,
                           page_size=1, num_pool_rows=num_pool_rows, num_decode=batch,
-                          width=((hi + 1 + 31) // 32) * 32)
+                          width=((hi + 1 + 31) // 32) * 32, page_order=page_order)
 
 
 def mixed_page64(seed: int = 1005, ndec: int = 64, dec_lo: int = 1024, dec_hi: int = 8192, next_: int = 4,
                  pre_hi: int = 4096, new_tokens: int = 2048, num_pool_rows: int = 1 << 20,
-                 page_size: int = 64) -> Workload:
+                 page_size: int = 64, page_order: str = "random") -> Workload:
     """page_size 64 mixed batch: decode requests first, then extend requests of
     `new_tokens` on prefixes ~ U{0..pre_hi}; page-aligned random free pages."""
     rng = _length_rng(seed)
@@ -86,7 +88,8 @@ def mixed_page64(seed: int = 1005, ndec: int = 64, dec_lo: int = 1024, dec_hi: i
     reqs += [RequestSpec(int(p), int(p) + new_tokens) for p in P]
     width = ((max(dec_hi + 1, pre_hi + new_tokens) + 31) // 32) * 32
     return build_workload("mixed_page64", seed, reqs, num_qo_heads=32, num_kv_heads=8, head_dim=128,
-                          page_size=page_size, num_pool_rows=num_pool_rows, num_decode=ndec, width=width)
+                          page_size=page_size, num_pool_rows=num_pool_rows, num_decode=ndec, width=width,
+                          page_order=page_order)
 
 
 FULL = {

@@ -149,11 +149,19 @@ class Workload:
                 f"s={self.page_size} N={self.num_pool_rows} W={self.width}")
 
 
-def _draw_pages(rng: np.random.Generator, num_pages: int, count: int) -> np.ndarray:
-    """`count` distinct free pages in random order, never page 0 (dummy) or the last page (poison)."""
+def _draw_pages(rng: np.random.Generator, num_pages: int, count: int, order: str = "random") -> np.ndarray:
+    """`count` distinct free pages, never page 0 (dummy) or the last page (poison).
+
+    order "random": a seeded random order of all free pages (rows scattered over
+    the whole pool, as after long churn).  order "sequential": pages 1, 2, ... in
+    allocation order, as a fresh pool's free list hands them out."""
     free = num_pages - 2
     if count > free:
         raise ValueError(f"pool too small: need {count} pages, have {free} free")
+    if order == "sequential":
+        return np.arange(1, count + 1, dtype=np.int64)
+    if order != "random":
+        raise ValueError(f"unknown page order {order!r}")
     if free <= (1 << 24):
         return rng.permutation(free)[:count].astype(np.int64) + 1
     return rng.choice(free, size=count, replace=False, shuffle=True).astype(np.int64) + 1
@@ -161,7 +169,8 @@ def _draw_pages(rng: np.random.Generator, num_pages: int, count: int) -> np.ndar
 
 def build_workload(name: str, seed: int, reqs: List[RequestSpec], *, num_qo_heads: int, num_kv_heads: int,
                    head_dim: int, page_size: int, num_pool_rows: int, num_decode: int,
-                   width: Optional[int] = None, spare_table_rows: int = 1, threads: int = 8) -> Workload:
+                   width: Optional[int] = None, spare_table_rows: int = 1, threads: int = 8,
+                   page_order: str = "random") -> Workload:
     """Lay out a batch in a paged pool and draw its values.
 
     Physical layout: a shared prefix (if any request has ``shared_prefix``) gets
@@ -200,7 +209,7 @@ def build_workload(name: str, seed: int, reqs: List[RequestSpec], *, num_qo_head
     new_pages = {i: math.ceil(reqs[i].device_len / s) - math.ceil(reqs[i].cached_len / s) for i in real}
     total = shared_pages + sum(priv_cached.values()) + sum(new_pages.values())
     rng_pages = np.random.Generator(np.random.PCG64(ss_pages))
-    order = _draw_pages(rng_pages, num_pages, total)
+    order = _draw_pages(rng_pages, num_pages, total, page_order)
     cur = 0
     shared_list = order[cur:cur + shared_pages]; cur += shared_pages
     req_cached_pages, req_new_pages = {}, {}
