@@ -69,9 +69,9 @@ extern "C" {
 
 /* ---- data structures ---------------------------------------------------- */
 
-/* One layer's KV pool: "each layer's K/V buffer is a (pages*page_size,
- * kv_heads, head_dim) token-row array; a token's physical position is its row
- * number" (learning notes, KV-pool passage; deep dive 6.2).
+/* One layer's KV pool (learning notes, KV-pool passage; deep dive 6.2): each
+ * of K and V is an array of token rows of shape (pages * page_size, kv_heads,
+ * head_dim), and a token's physical position is simply its row number.
  * Element (row r, KV head g, dim e) of K is at k + (r*row_stride + g*head_dim + e)
  * bf16 elements; the same for V.  Page p owns rows [p*page_size, (p+1)*page_size). */
 typedef struct pkv_kv_pool {
@@ -186,8 +186,8 @@ int build_attn_metadata(const pkv_batch* batch, const pkv_page_table* page_table
 /* paged_decode_attn: for each decode request i < num_decode and query head h,
  *   o[qo_indptr[i], h] = softmax(sm_scale * q[qo_indptr[i], h] . K[rows]^T) V[rows]
  * over rows = page_table[table_idx[i], 0 .. device_len[i]) (the new row stored
- * by kv_store included), gathered through the page table.  Split-K
- * ("parallelise across KV", learning notes kernel passage; flash-decoding):
+ * by kv_store included), gathered through the page table.  Split-K over the
+ * keys (learning notes kernel passage; flash-decoding):
  * the (request, group of KV heads, 32-key tile) work is split evenly over a
  * fixed set of runs of wavefronts, so a request's keys may be shared by
  * several of them, and a merge kernel combines their partial softmax states.
