@@ -77,6 +77,7 @@ struct MetaArgs {
   int32_t* status;
   char* plan;
   PlanLayout layout;
+  int32_t fuse_tokens;  // 1: plan_kernel also maps the tokens (small batches; see launch_metadata)
 };
 
 struct AttnArgs {

@@ -19,6 +19,9 @@
 //   token_kernel (one thread per new token): finds its request by binary
 //                search over qo_indptr and writes page_table, out_loc and
 //                positions.
+// For a small batch (at most kFuseTokens new tokens and kFuseReqs requests)
+// plan_kernel maps the tokens itself, from an LDS copy of qo_indptr, and the
+// second launch and the gap before it are saved.
 // Integer work only; results are bit-exact by construction.
 #include "kernels.hpp"
 
@@ -30,6 +33,8 @@ constexpr int kPlanThreads = 256;
 constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kScanVals = 5;
 constexpr int kSortBuckets = 1024;  // extend tiles sorted by key count in steps of 64 keys (capped)
+constexpr int kFuseTokens = 512;    // new tokens plan_kernel maps itself
+constexpr int kFuseReqs = 1024;     // requests of such a batch (an LDS copy of qo_indptr)
 static_assert(kSortBuckets % kPlanThreads == 0, "whole buckets per thread");
 
 struct ReqInfo {
@@ -84,8 +89,76 @@ __device__ inline void block_scan(int32_t (&v)[kScanVals], int32_t (&excl)[kScan
   __syncthreads();
 }
 
+// Token t of the batch (t < T): its request i (qo[i] <= t < qo[i + 1], by
+// binary search over qo, the running totals in global memory or LDS), its
+// logical position, and its row in the request's partial page or new pages;
+// writes page_table, out_loc and positions.  A token that gets no row is
+// marked -1 in out_loc and positions, so the store and RoPE calls skip it
+// instead of reusing a stale row.
+__device__ inline void map_token(const MetaArgs& a, int64_t t, const int32_t* qo, const int32_t* alloc_ptr) {
+  auto unmapped = [&]() {
+    a.out_loc[t] = -1;
+    a.positions[t] = -1;
+  };
+  if (t >= qo[a.B]) {  // fewer new tokens than num_tokens (flagged by plan_kernel)
+    unmapped();
+    return;
+  }
+  int lo = 0, hi = a.B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (qo[mid] <= t) lo = mid;
+    else hi = mid;
+  }
+  const int i = lo;
+  int32_t bits = 0;
+  if (!request_ok(a, i, &bits)) {  // already reported by plan_kernel
+    unmapped();
+    return;
+  }
+  const int32_t r = a.table_idx[i];
+  const int32_t c = a.cached_len[i];
+  const int32_t j = c + (int32_t)(t - qo[i]);
+  const int32_t s = a.page_shift;
+  const int32_t slot = j & ((1 << s) - 1);
+  const int32_t first_new_page = ceil_div_pow2(c, s);
+  const int32_t lp = j >> s;
+  int64_t row;
+  int32_t* pt_row = a.page_table + (int64_t)r * a.W;
+  if (lp < first_new_page) {
+    // the request's partially filled last cached page
+    row = (int64_t)pt_row[j - slot] + slot;
+    if (row < 0 || row >= a.num_pool_rows) bits |= PKV_STATUS_BAD_PAGE_ROW;
+  } else {
+    const int64_t ai = (int64_t)alloc_ptr[i] + (lp - first_new_page);
+    if (ai >= a.num_alloc) {
+      bits |= PKV_STATUS_BAD_ALLOC;
+      row = -1;
+    } else {
+      const int32_t pr = a.alloc_rows[ai];
+      row = (int64_t)pr + slot;
+      if (pr < 0 || (pr & ((1 << s) - 1)) != 0 || row >= a.num_pool_rows) bits |= PKV_STATUS_BAD_ALLOC;
+    }
+  }
+  if (bits) {
+    raise_status(a.status, bits);
+    unmapped();
+    return;
+  }
+  pt_row[j] = (int32_t)row;
+  a.out_loc[t] = (int32_t)row;
+  a.positions[t] = j;
+}
+
+__global__ void __launch_bounds__(256) token_kernel(MetaArgs a) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= a.T) return;
+  map_token(a, t, a.qo_indptr, (const int32_t*)(a.plan + a.layout.alloc_ptr_off));
+}
+
 __global__ void __launch_bounds__(kPlanThreads) plan_kernel(MetaArgs a) {
   __shared__ int32_t smem[kScanVals][kPlanWaves];
+  __shared__ int32_t s_qo[kFuseReqs + 1];  // qo_indptr of a fused batch
   const int tid = threadIdx.x;
   int32_t bits = 0;
   int32_t* header = (int32_t*)a.plan;
@@ -103,6 +176,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(MetaArgs a) {
     a.kv_indptr[0] = 0;
     dec_tile_ptr[0] = 0;
     alloc_ptr[0] = 0;
+    s_qo[0] = 0;
   }
   for (int base = 0; base < a.B; base += kPlanThreads) {
     const int i = base + tid;
@@ -125,6 +199,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(MetaArgs a) {
     if (i < a.B) {
       const int32_t qo_end = carry[0] + ex[0] + ri.ext;
       a.qo_indptr[i + 1] = qo_end;
+      if (a.fuse_tokens) s_qo[i + 1] = qo_end;
       a.kv_indptr[i + 1] = carry[1] + ex[1] + ri.dl;
       a.last_indices[i] = qo_end - 1;
       alloc_ptr[i + 1] = carry[2] + ex[2] + ri.new_pages;
@@ -198,75 +273,22 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(MetaArgs a) {
     const int2 tt = tiles_raw[t];
     tiles[atomicAdd(&bucket[tile_bucket(tt)], 1)] = tt;
   }
-}
-
-__global__ void __launch_bounds__(256) token_kernel(MetaArgs a) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= a.T) return;
-  const int32_t* alloc_ptr = (const int32_t*)(a.plan + a.layout.alloc_ptr_off);
-  // A token that gets no row is marked -1 in out_loc and positions, so the
-  // store and RoPE calls skip it instead of reusing a stale row.
-  auto unmapped = [&]() {
-    a.out_loc[t] = -1;
-    a.positions[t] = -1;
-  };
-  if (t >= a.qo_indptr[a.B]) {  // fewer new tokens than num_tokens (flagged by plan_kernel)
-    unmapped();
-    return;
+  if (a.fuse_tokens) {
+    // the alloc offsets other threads wrote to global memory, and s_qo
+    __threadfence_block();
+    __syncthreads();
+    for (int64_t t = tid; t < a.T; t += kPlanThreads) map_token(a, t, s_qo, alloc_ptr);
   }
-  // request i: qo_indptr[i] <= t < qo_indptr[i + 1]
-  int lo = 0, hi = a.B;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.qo_indptr[mid] <= t) lo = mid;
-    else hi = mid;
-  }
-  const int i = lo;
-  int32_t bits = 0;
-  if (!request_ok(a, i, &bits)) {  // already reported by plan_kernel
-    unmapped();
-    return;
-  }
-  const int32_t r = a.table_idx[i];
-  const int32_t c = a.cached_len[i];
-  const int32_t j = c + (int32_t)(t - a.qo_indptr[i]);
-  const int32_t s = a.page_shift;
-  const int32_t slot = j & ((1 << s) - 1);
-  const int32_t first_new_page = ceil_div_pow2(c, s);
-  const int32_t lp = j >> s;
-  int64_t row;
-  int32_t* pt_row = a.page_table + (int64_t)r * a.W;
-  if (lp < first_new_page) {
-    // the request's partially filled last cached page
-    row = (int64_t)pt_row[j - slot] + slot;
-    if (row < 0 || row >= a.num_pool_rows) bits |= PKV_STATUS_BAD_PAGE_ROW;
-  } else {
-    const int64_t ai = (int64_t)alloc_ptr[i] + (lp - first_new_page);
-    if (ai >= a.num_alloc) {
-      bits |= PKV_STATUS_BAD_ALLOC;
-      row = -1;
-    } else {
-      const int32_t pr = a.alloc_rows[ai];
-      row = (int64_t)pr + slot;
-      if (pr < 0 || (pr & ((1 << s) - 1)) != 0 || row >= a.num_pool_rows) bits |= PKV_STATUS_BAD_ALLOC;
-    }
-  }
-  if (bits) {
-    raise_status(a.status, bits);
-    unmapped();
-    return;
-  }
-  pt_row[j] = (int32_t)row;
-  a.out_loc[t] = (int32_t)row;
-  a.positions[t] = j;
 }
 
 }  // namespace
 
-hipError_t launch_metadata(const MetaArgs& a, hipStream_t s) {
+hipError_t launch_metadata(const MetaArgs& a_in, hipStream_t s) {
+  MetaArgs a = a_in;
+  a.fuse_tokens = (a.T <= kFuseTokens && a.B <= kFuseReqs) ? 1 : 0;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.T == 0) return e;
+  if (e != hipSuccess || a.T == 0 || a.fuse_tokens) return e;
   const int64_t blocks = (a.T + 255) / 256;
   hipLaunchKernelGGL(token_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
