@@ -170,6 +170,14 @@ def _edge_workloads():
     cases.append(("seq_pages64", configs.mixed_page64(seed=61, ndec=6, dec_lo=1, dec_hi=300, next_=3, pre_hi=200,
                                                       new_tokens=150, num_pool_rows=64 * 64,
                                                       page_order="sequential")))
+    # batches at the size where build_attn_metadata stops mapping the tokens inside its
+    # one-workgroup plan kernel (512 new tokens) and launches a kernel for them
+    for nreq in (512, 513):
+        lens = [(37 * k) % 300 + 1 for k in range(nreq)]
+        reqs = [RequestSpec(l, l + 1) for l in lens]
+        cases.append((f"meta{nreq}", build_workload(f"meta{nreq}", 62 + nreq % 2, reqs, num_qo_heads=32,
+                                                    num_kv_heads=8, head_dim=128, page_size=1,
+                                                    num_pool_rows=1 << 18, num_decode=nreq)))
     # one long decode request spread over many splits, width exactly its length rounded to 32
     cases.append(("long_single", build_workload("long_single", 50, [RequestSpec(20000, 20001)],
                                                 num_qo_heads=64, num_kv_heads=8, head_dim=128, page_size=1,
