@@ -238,40 +238,42 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(MetaArgs a) {
   // order).  The order inside a bucket is whatever the LDS atomics give;
   // every tile's result is independent of it.
   __shared__ int32_t bucket[kSortBuckets];
-  const int32_t n_t = min(carry[4], a.layout.cap_tiles);
-  auto tile_bucket = [&](int2 t) -> int {
-    const int32_t ci = a.cached_len[t.x];
-    const int32_t di = a.device_len[t.x];
-    const int32_t kv_end = min(di, ci + t.y + tq);
-    return kSortBuckets - 1 - min(max(kv_end, 0) >> 6, kSortBuckets - 1);
-  };
-  for (int b = tid; b < kSortBuckets; b += kPlanThreads) bucket[b] = 0;
-  __syncthreads();  // also orders the tiles_raw writes above before the reads below
-  for (int t = tid; t < n_t; t += kPlanThreads) atomicAdd(&bucket[tile_bucket(tiles_raw[t])], 1);
-  __syncthreads();
-  {
-    constexpr int kPer = kSortBuckets / kPlanThreads;
-    int32_t cnt[kPer];
-    int32_t mine = 0;
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      cnt[q] = bucket[tid * kPer + q];
-      mine += cnt[q];
+  const int32_t n_t = min(carry[4], a.layout.cap_tiles);  // the same in every thread
+  if (n_t > 0) {  // decode-only batches skip the sort
+    auto tile_bucket = [&](int2 t) -> int {
+      const int32_t ci = a.cached_len[t.x];
+      const int32_t di = a.device_len[t.x];
+      const int32_t kv_end = min(di, ci + t.y + tq);
+      return kSortBuckets - 1 - min(max(kv_end, 0) >> 6, kSortBuckets - 1);
+    };
+    for (int b = tid; b < kSortBuckets; b += kPlanThreads) bucket[b] = 0;
+    __syncthreads();  // also orders the tiles_raw writes above before the reads below
+    for (int t = tid; t < n_t; t += kPlanThreads) atomicAdd(&bucket[tile_bucket(tiles_raw[t])], 1);
+    __syncthreads();
+    {
+      constexpr int kPer = kSortBuckets / kPlanThreads;
+      int32_t cnt[kPer];
+      int32_t mine = 0;
+  #pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        cnt[q] = bucket[tid * kPer + q];
+        mine += cnt[q];
+      }
+      int32_t v[kScanVals] = {mine, 0, 0, 0, 0};
+      int32_t ex[kScanVals], tot[kScanVals];
+      block_scan(v, ex, tot, smem);
+      int32_t run = ex[0];
+  #pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        bucket[tid * kPer + q] = run;  // first position of the bucket
+        run += cnt[q];
+      }
     }
-    int32_t v[kScanVals] = {mine, 0, 0, 0, 0};
-    int32_t ex[kScanVals], tot[kScanVals];
-    block_scan(v, ex, tot, smem);
-    int32_t run = ex[0];
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      bucket[tid * kPer + q] = run;  // first position of the bucket
-      run += cnt[q];
+    __syncthreads();
+    for (int t = tid; t < n_t; t += kPlanThreads) {
+      const int2 tt = tiles_raw[t];
+      tiles[atomicAdd(&bucket[tile_bucket(tt)], 1)] = tt;
     }
-  }
-  __syncthreads();
-  for (int t = tid; t < n_t; t += kPlanThreads) {
-    const int2 tt = tiles_raw[t];
-    tiles[atomicAdd(&bucket[tile_bucket(tt)], 1)] = tt;
   }
   if (a.fuse_tokens) {
     // the alloc offsets other threads wrote to global memory, and s_qo
