@@ -122,6 +122,30 @@ def test_planted_spikes(kind):
     ds.free()
 
 
+@pytest.mark.parametrize("which", ["small5", "full3"])
+def test_attention_repeated_on_one_plan(which):
+    """The attention calls run again on the same metadata (as every layer of a
+    model does) give the same results each time: state they keep in the plan
+    between workgroups is back at its start when a call ends."""
+    if which == "small5":
+        w, ext = configs.small(5), None
+    else:
+        w = configs.FULL[3]()
+        ext = P.sample_tokens(w, per_request=4, seed=33)
+    ds, ref, _ = run_case(w, extend_tokens=ext, label=f"repeat {which}")
+    for r in range(3):
+        ds.o.fill_(float("nan"))
+        if w.num_decode:
+            ds.decode()
+        ds.extend()
+        torch.cuda.synchronize()
+        assert ds.status() == 0
+        P.real_outputs_finite(ds, w)
+        stats = P.check_attention(ds, ref["out"], w, f"repeat {which} call {r + 2}")
+        log(f"  call {r + 2} ok {stats}")
+    ds.free()
+
+
 def _edge_workloads():
     cases = []
     # every request has a single key: the output is that key's V, exactly
