@@ -53,6 +53,7 @@ namespace pkv {
 namespace {
 
 constexpr int kKeyTile = 64;
+constexpr int kVW = 4;  // V^T operand reads in flight ahead of the PV MFMAs
 constexpr int kKsStride = 136;  // bf16 elements per K row in LDS (128 + 8 pad)
 constexpr int kVsStride = 160;  // bf16 elements per V row in LDS (80 dwords: 4 rows x 16 dwords hit 64 distinct banks)
 constexpr int kWaves = 8;
@@ -196,16 +197,15 @@ __global__ void __launch_bounds__(64 * kWaves, 8 / kWaves) extend_kernel(AttnArg
   auto key_tile = [&](int kt, auto set_tag) __attribute__((always_inline)) {
     constexpr int SET = decltype(set_tag)::value;
     const bool MASK = kt >= kt_mask;  // uniform
-    // the next tile goes to the other stage (last read before the previous
-    // barrier); its register set then receives the tile three ahead
-    store_tile(kt + kKeyTile, std::integral_constant<int, SET ^ 1>{});
-    gather(kt + 3 * kKeyTile, std::integral_constant<int, SET ^ 1>{});
     const uint16_t* ks = ks_all[SET];
     const uint16_t* vs = vs_all[SET];
 
     // S^T = K Q^T : two 32-key blocks (raw scores, scale folded into exp below);
     // the two accumulation chains alternate and the K operands are read from
-    // LDS four MFMAs ahead
+    // LDS four MFMAs ahead, the first four before the next tile's store and
+    // gathers.  sched_barrier pins that order: left to itself the compiler
+    // issued each read about one MFMA before its use and every MFMA waited
+    // for the LDS latency (3.7% of the launch on the shared-prefix batch).
     f32x16 sacc[2];
     auto kread = [&](int j) __attribute__((always_inline)) {
       return as_bf16x8(*reinterpret_cast<const uint4*>(&ks[((j & 1) * 32 + l32) * kKsStride + half * 8 + 16 * (j >> 1)]));
@@ -213,11 +213,18 @@ __global__ void __launch_bounds__(64 * kWaves, 8 / kWaves) extend_kernel(AttnArg
     bf16x8 kb[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) kb[j] = kread(j);
+    __builtin_amdgcn_sched_barrier(0);
+    // the next tile goes to the other stage (last read before the previous
+    // barrier); its register set then receives the tile three ahead
+    store_tile(kt + kKeyTile, std::integral_constant<int, SET ^ 1>{});
+    gather(kt + 3 * kKeyTile, std::integral_constant<int, SET ^ 1>{});
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int mb = j & 1, kk = j >> 1;
       sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[j & 3], qop[kk], kk == 0 ? f32x16{} : sacc[mb], 0, 0, 0);
       if (j + 4 < 16) kb[j & 3] = kread(j + 4);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // element v of block mb is key kt + 32 mb + 8 (v / 4) + 4 half + v % 4 of row l32
     if (MASK) {
@@ -236,6 +243,23 @@ __global__ void __launch_bounds__(64 * kWaves, 8 / kWaves) extend_kernel(AttnArg
     // a tile whose scores grew by more than 64 (log2 units) since the last max
     // take the slow path: the true tile max (both lane halves of a row), the
     // rescale of the accumulator and sum, and the probabilities again.
+    // V^T operand of PV MFMA m (numbered below): slots 0..3 are keys key0 +
+    // 0..3, slots 4..7 keys key0 + 8..11.  The first kVW are read before the
+    // softmax, so their latency is hidden behind it.
+    auto vread = [&](int m) __attribute__((always_inline)) {
+      const int mb = m >> 3, kq = (m >> 2) & 1, nb = m & 3;
+      const int key0 = mb * 32 + 16 * kq + 4 * half;
+      const int j16 = lane & 15;
+      const uint16_t* vp = &vs[(key0 + (j16 >> 2)) * kVsStride + nb * 32 + ((lane >> 4) & 1) * 16 + 4 * (j16 & 3)];
+      const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)vp);
+      const v4s r2 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(vp + 8 * kVsStride));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(r1, r2, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8 vb[kVW];
+#pragma unroll
+    for (int m = 0; m < kVW; ++m) vb[m] = vread(m);
+    __builtin_amdgcn_sched_barrier(0);
     uint32_t pk[2][8];  // bf16 pairs: block mb, words 4 kq + 0..3
     float psum0, psum1;
     auto make_p = [&](float nms) __attribute__((always_inline)) {
@@ -275,25 +299,16 @@ __global__ void __launch_bounds__(64 * kWaves, 8 / kWaves) extend_kernel(AttnArg
       make_p(m == -INFINITY ? 0.f : -m);
     }
 
-    // O^T += V^T P^T, 16 keys per MFMA
+    // O^T += V^T P^T, 16 keys per MFMA: MFMA m = 4 (2 mb + kq) + nb; its V^T
+    // operand is read kVW MFMAs ahead, in an order pinned as for S
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int kq = 0; kq < 2; ++kq) {
-        const bf16x8 pop = as_bf16x8(make_uint4(pk[mb][4 * kq], pk[mb][4 * kq + 1], pk[mb][4 * kq + 2], pk[mb][4 * kq + 3]));
-        // V^T operand: slots 0..3 are keys key0 + 0..3, slots 4..7 keys key0 + 8..11
-        const int key0 = mb * 32 + 16 * kq + 4 * half;
-        const int j16 = lane & 15;
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const uint16_t* vp = &vs[(key0 + (j16 >> 2)) * kVsStride + nb * 32 + ((lane >> 4) & 1) * 16 + 4 * (j16 & 3)];
-          const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)vp);
-          const v4s r2 =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(vp + 8 * kVsStride));
-          const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r1, r2, 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, oacc[nb], 0, 0, 0);
-        }
-      }
+    for (int m = 0; m < 16; ++m) {
+      const int mb = m >> 3, kq = (m >> 2) & 1, nb = m & 3;
+      const bf16x8 pop = as_bf16x8(make_uint4(pk[mb][4 * kq], pk[mb][4 * kq + 1], pk[mb][4 * kq + 2], pk[mb][4 * kq + 3]));
+      oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[m % kVW], pop, oacc[nb], 0, 0, 0);
+      if (m + kVW < 16) vb[m % kVW] = vread(m + kVW);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     lsum = lsum * alpha + (psum0 + psum1);
   };
 
