@@ -18,16 +18,21 @@ __global__ void __launch_bounds__(256) kv_store_kernel(StoreArgs a) {
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += stride) {
     const int64_t t = idx / a.row_vec;
     const int32_t c = (int32_t)(idx - t * a.row_vec);
-    const int32_t row = a.out_loc[t];
+    int32_t row = a.out_loc[t];
+    // the source vectors do not depend on the row: their loads go out with
+    // the out_loc load, so a thread waits for one memory round trip, not two
+    const int64_t src = t * a.row_vec + c;
+    uint4 kv = a.k_new[src];
+    uint4 vv = a.v_new[src];
+    // keeps the loads above the branch (the compiler would sink them into it)
+    asm volatile("" : "+v"(row), "+v"(kv.x), "+v"(kv.y), "+v"(kv.z), "+v"(kv.w), "+v"(vv.x), "+v"(vv.y), "+v"(vv.z),
+                 "+v"(vv.w));
     if (row < 0 || (int64_t)row >= a.num_rows) {
       // -1 marks a token build_attn_metadata could not map (already reported)
       if (c == 0 && row != -1) raise_status(a.status, PKV_STATUS_BAD_OUT_LOC);
       continue;
     }
     const int64_t dst = (int64_t)row * a.row_stride_vec + c;
-    const int64_t src = t * a.row_vec + c;
-    const uint4 kv = a.k_new[src];
-    const uint4 vv = a.v_new[src];
     a.k_pool[dst] = kv;
     a.v_pool[dst] = vv;
   }
