@@ -3,16 +3,26 @@
 
 One step = one pass of the whole path over one batch: build_attn_metadata,
 kv_store, paged_decode_attn (split-K partial + merge) and paged_extend_attn,
-on inputs already resident in HBM.  The default workload is the serving
-decode batch (Llama-3-8B-like layer: 32 query / 8 KV heads, head_dim 128,
-256 requests = 200 real + 56 padding, contexts U[512, 4096], page_size 1,
-2^21-row pool).  `--config 1..5` selects another of the five workloads.
+on inputs already resident in HBM.  The default run measures, in this order:
 
-Prints ONE JSON line.  `value` is the whole step's algorithmic bytes (decode
-K/V + page-table + q/o, store, metadata) per second for decode-dominated
-workloads, or its extend flops per second for extend-dominated ones.
-`roofline` covers the dominant call, timed with HIP events on the stream it
-runs on; `cpu_baseline` times the fp64 oracle on the host.
+  1  tiny decode (latency only: eager step against one graph replay),
+  2  serving decode (Llama-3-8B-like layer: 32 query / 8 KV heads, head_dim
+     128, 256 requests = 200 real + 56 padding, contexts U[512, 4096], page
+     size 1, 2^21-row pool) - the headline `value`,
+  3  chunked-prefill extend on a radix-shared 2048-row prefix (8 x 1024 new
+     tokens) - the extend half of the metric (`extend`, `roofline_extend`),
+  5  the page-size-64 mixed batch (64 decode + 4 extend requests),
+  4  long-context decode (64 query / 8 KV heads, 16K-32K keys, 150 GB pool),
+
+and prints ONE JSON line.  `--config N` measures one workload only.
+
+Timing: K steps, each preceded (outside the timed region) by a pass that
+reads a 1 GiB buffer, so L2 and the 256 MB MALL hold none of the step's data
+and no dirty lines that the timed launch would have to write back; HIP events
+on the launch stream; medians over the K steps.  Extend is also timed without
+the flush (back-to-back steps), reported beside the flushed figure.
+`roofline` / `roofline_extend` cover the dominant call of workloads 2 and 3;
+`cpu_baseline` / `cpu_baseline_extend` time the fp64 oracle on the host.
 """
 from __future__ import annotations
 
@@ -41,15 +51,32 @@ WORKLOAD_TEXT = {
     5: "mixed_page64: 32 q / 8 kv heads, d 128, page_size 64, 64 decode (ctx U[1024,8192]) + 4 extend "
        "(2048 new tokens on prefixes U[0,4096]), pool 2^20 rows",
 }
+DEFAULT_CONFIGS = "1,2,3,5,4"
+FLUSH_BYTES = 1 << 30
 
 
 def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
+def host_description() -> dict:
+    """The host cores the CPU baseline runs on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "usable_cores": len(os.sched_getaffinity(0)), "os_cpu_count": os.cpu_count()}
+
+
 def cpu_baseline(w, kind: str, budget_s: float):
-    """The fp64 oracle as it stands, single BLAS thread, on a bounded sample."""
-    from threadpoolctl import threadpool_limits
+    """The fp64 oracle as it stands, on one core (one BLAS thread), on a
+    bounded sample of the workload."""
+    from threadpoolctl import threadpool_info, threadpool_limits
     import oracle.pagedkv_oracle as O
     from oracle.run import initial_pool
     from paged_kv_attention_08_amd import perf_model as PM
@@ -57,11 +84,12 @@ def cpu_baseline(w, kind: str, budget_s: float):
     pool = initial_pool(w)
     real = [i for i in range(w.num_reqs) if not w.is_padding[i]]
     with threadpool_limits(limits=1):
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
         t0 = time.perf_counter()
         meta = O.build_metadata(w.page_table, w.table_idx, w.cached_len, w.device_len, w.alloc_rows, w.page_size)
         pool2 = O.store_kv(pool, w.k_new, w.v_new, meta["out_loc"])
         t_fixed = time.perf_counter() - t0
-        done_reqs, done_tokens = [], {}
+        done_reqs = []
         t1 = time.perf_counter()
         if kind == "decode":
             for i in real:
@@ -96,8 +124,8 @@ def cpu_baseline(w, kind: str, budget_s: float):
             value = flops / elapsed / 1e12
             unit = "TFLOP/s"
             sample = f"extend attention of {n_tok} randomly drawn new tokens (all query heads each)"
-    return {"value": value, "unit": unit, "cores": 1, "kind": "oracle", "sample": sample,
-            "seconds": round(elapsed, 2)}
+    return {"value": round(value, 4), "unit": unit, "cores": 1, "kind": "oracle", "sample": sample,
+            "seconds": round(elapsed, 2), "blas_threads": blas_threads}
 
 
 def graph_measurement(ds, w, args, stream):
@@ -188,7 +216,7 @@ def rope_measurement(ds, w, args, stream, PM):
     cache = torch.empty((max_pos, w.head_dim), dtype=torch.float32, device="cuda")
     pkv.rope_cos_sin_cache(cache, 1e6)
     inp = rope_inputs(7, 1, w.num_qo_heads, w.num_kv_heads, w.head_dim)  # only the norm weights are used
-    from tests.gpu_harness import bf16_tensor
+    from paged_kv_attention_08_amd.device_step import bf16_tensor
     norm = (bf16_tensor(inp.q_weight, "cuda"), bf16_tensor(inp.k_weight, "cuda"), NORM_EPS)
     out_loc, positions = ds.meta.out_loc[:T], ds.meta.positions[:T]
 
@@ -214,6 +242,149 @@ def rope_measurement(ds, w, args, stream, PM):
             "what": "RoPE base 1e6 + per-head q/k RMS norm fused into the K/V store"}
 
 
+def measure(cfg, args, torch, flush_buf):
+    """Every timing of one workload.  Returns (summary, roofline, dominant call)."""
+    from workloads import configs
+    from paged_kv_attention_08_amd.device_step import DeviceStep
+    from paged_kv_attention_08_amd import perf_model as PM
+    from paged_kv_attention_08_amd import profiling
+    import paged_kv_attention_08_amd as pkv
+
+    log(f"config {cfg}: generating")
+    w = configs.FULL[cfg](page_order=args.page_order)
+    log(w.summary())
+    pool = None
+    if args.layers > 1 or args.layout != "layer_first":
+        layout = {"layer_first": pkv.KVCacheTensors.LAYER_FIRST, "page_first": pkv.KVCacheTensors.PAGE_FIRST,
+                  "row_interleaved": pkv.KVCacheTensors.ROW_INTERLEAVED}[args.layout]
+        cache = pkv.KVCacheTensors(args.layers, w.num_pool_rows, w.num_kv_heads, w.head_dim, w.page_size, layout)
+        pool = cache.layer(0)
+    ds = DeviceStep(w, pool=pool)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    has_decode = w.num_decode > 0
+    has_extend = w.num_decode < w.num_reqs
+
+    def step(marks):
+        """One pass of the path; marks maps a position (0..3 before metadata,
+        store, decode and extend, 4 after the last call) to an event."""
+        def mark(j):
+            e = marks.get(j)
+            if e is not None:
+                e.record(stream)
+        mark(0)
+        ds.metadata()
+        mark(1)
+        ds.store()
+        mark(2)
+        if has_decode:
+            ds.decode()
+        mark(3)
+        if has_extend:
+            ds.extend()
+        mark(4)
+
+    def flush():
+        if flush_buf is not None:
+            flush_buf.sum()  # a read pass: evicts L2 and the MALL, leaves no dirty lines
+
+    for _ in range(args.warmup):
+        step({})
+    torch.cuda.synchronize()
+    # Under a fresh load the GPU runs at lower clocks for its first ~100 ms;
+    # untimed steps until the clocks have settled.
+    settle = 0
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(8):
+            step({})
+        torch.cuda.synchronize()
+        settle += 8
+    assert ds.status() == 0, f"device status {ds.status():#x}"
+
+    def timed_pass(positions, flushed):
+        """K steps with events at `positions`; per step the durations between
+        consecutive marks (ms)."""
+        evs = [{j: torch.cuda.Event(enable_timing=True) for j in positions} for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for k in range(args.steps):
+            if flushed:
+                flush()
+            step(evs[k])
+        torch.cuda.synchronize()
+        return np.array([[evs[k][a].elapsed_time(evs[k][b]) for a, b in zip(positions[:-1], positions[1:])]
+                         for k in range(args.steps)])
+
+    flushed = flush_buf is not None
+    step_ms = float(np.median(timed_pass([0, 4], flushed)[:, 0]))
+    parts = np.median(timed_pass([0, 1, 2, 3, 4], flushed), axis=0)  # metadata, store, decode, extend
+    decode_dominant = has_decode and (not has_extend or parts[2] >= parts[3])
+    dom = (2, 3) if decode_dominant else (3, 4)
+    dom_ms = float(np.median(timed_pass(list(dom), flushed)[:, 0]))
+    unflushed_ms = float(np.median(timed_pass(list(dom), False)[:, 0])) if flushed else dom_ms
+    assert ds.status() == 0, f"device status {ds.status():#x}"
+
+    real = ~w.is_padding
+    dec_mask = np.zeros(w.num_reqs, dtype=bool)
+    dec_mask[:w.num_decode] = True
+    dec_bytes = PM.decode_bytes(w.device_len[dec_mask & real], w.num_qo_heads, w.num_kv_heads, w.head_dim,
+                                w.page_size)
+    st_bytes = PM.store_bytes(int((w.device_len[real] - w.cached_len[real]).sum()), w.num_kv_heads, w.head_dim)
+    md_bytes = PM.metadata_bytes(w.num_reqs, w.num_tokens)
+    ext_flops = PM.extend_flops(w.cached_len[~dec_mask], w.device_len[~dec_mask], w.num_qo_heads, w.head_dim)
+    call = "paged_decode_attn" if decode_dominant else "paged_extend_attn"
+    measured = profiling.traffic_for(call, cfg)  # None unless taken on the current kernel sources
+    traffic = None if measured is None else round(measured["traffic_bytes"])
+    profile = None if measured is None else measured["summary"]
+    decode_ms = dom_ms if decode_dominant else float(parts[2])
+    extend_ms = dom_ms if not decode_dominant else float(parts[3])
+    out = {"workload": WORKLOAD_TEXT[cfg], "step_ms": round(step_ms, 4),
+           "calls_ms": {"metadata": round(float(parts[0]), 4), "kv_store": round(float(parts[1]), 4),
+                        "decode": round(decode_ms, 4) if has_decode else None,
+                        "extend": round(extend_ms, 4) if has_extend else None},
+           "settle_steps": settle}
+    if has_decode:
+        gbps = dec_bytes / (decode_ms * 1e-3) / 1e9
+        out["decode_gbps"] = round(gbps, 1)
+        out["decode_frac_hbm"] = round(gbps / PM.HBM_PEAK_GBPS, 4)
+    if has_extend:
+        tf = ext_flops / (extend_ms * 1e-3) / 1e12
+        out["extend_tflops"] = round(tf, 1)
+        out["extend_frac_mfma"] = round(tf / PM.BF16_DENSE_PEAK_TFLOPS, 4)
+        if not decode_dominant:
+            tfu = ext_flops / (unflushed_ms * 1e-3) / 1e12
+            out["extend_unflushed_ms"] = round(unflushed_ms, 4)
+            out["extend_unflushed_frac_mfma"] = round(tfu / PM.BF16_DENSE_PEAK_TFLOPS, 4)
+    else:
+        out["decode_unflushed_ms"] = round(unflushed_ms, 4)
+    out["store_gbps"] = round(st_bytes / (float(parts[1]) * 1e-3) / 1e9, 1)
+    if decode_dominant:
+        roof = {"bound": "hbm", "achieved": out["decode_gbps"], "peak": PM.HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": out["decode_frac_hbm"], "traffic": traffic, "kernel": "decode_kernel + decode_merge_kernel",
+                "algorithmic_bytes_per_launch": dec_bytes, "avg_launch_ms": round(decode_ms, 4), "profile": profile}
+        out["step_gbps"] = round((dec_bytes + st_bytes + md_bytes) / (step_ms * 1e-3) / 1e9, 1)
+    else:
+        m = ~dec_mask
+        uniq = PM.extend_unique_bytes(w.page_table, w.table_idx[m], w.cached_len[m], w.device_len[m],
+                                      w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size)
+        roof = {"bound": "mfma", "achieved": out["extend_tflops"], "peak": PM.BF16_DENSE_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": out["extend_frac_mfma"], "traffic": traffic, "kernel": "extend_kernel",
+                "algorithmic_flops_per_launch": ext_flops, "algorithmic_bytes_per_launch": uniq,
+                "avg_launch_ms": round(extend_ms, 4), "profile": profile}
+        out["step_tflops"] = round(ext_flops / (step_ms * 1e-3) / 1e12, 1)
+    if args.graph and cfg in (1, 2):
+        out["decode_graph"] = graph_measurement(ds, w, args, stream)
+    if args.next_rows and cfg in (2, 3):
+        out["page_alloc"] = alloc_measurement(ds, w, args, stream)
+        out["kv_store_rope"] = rope_measurement(ds, w, args, stream, PM)
+    ds.free()
+    if args.cpu_budget > 0 and cfg != 1:
+        log(f"config {cfg}: cpu baseline (fp64 oracle)")
+        out["cpu_baseline"] = cpu_baseline(w, "decode" if decode_dominant else "extend", args.cpu_budget)
+    del w
+    return out, roof
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -221,10 +392,15 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="after the warm-up steps, untimed steps for at least this long (clock ramp)")
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--flush", action="store_true", help="flush L2/MALL before every step (outside the events)")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--configs", default=DEFAULT_CONFIGS,
+                    help="workloads to measure, in order (the headline value is workload 2's)")
+    ap.add_argument("--config", type=int, default=None, choices=[1, 2, 3, 4, 5],
+                    help="measure this one workload only (its own figures become the headline)")
+    ap.add_argument("--no-flush", action="store_true", help="no L2/MALL flush before the timed steps")
+    ap.add_argument("--cpu-budget", type=float, default=8.0, help="seconds of oracle work per workload (0: none)")
+    ap.add_argument("--no-next-rows", dest="next_rows", action="store_false",
+                    help="skip the allocator and RoPE-store measurements")
+    ap.add_argument("--no-graph", dest="graph", action="store_false", help="skip the decode graph measurements")
     ap.add_argument("--layout", choices=["layer_first", "page_first", "row_interleaved"], default="layer_first",
                     help="physical order of a multi-layer KV cache whose layer 0 the step runs on")
     ap.add_argument("--layers", type=int, default=1, help="layers in that cache (1: a plain one-layer pool)")
@@ -243,9 +419,6 @@ def main(argv=None):
         return 2
 
     import torch
-    from workloads import configs
-    from tests.gpu_harness import DeviceStep
-    from paged_kv_attention_08_amd import perf_model as PM
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -261,164 +434,44 @@ def main(argv=None):
         print(json.dumps({"copy_calibration_bytes_read": nbytes, "copy_calibration_bytes_written": nbytes,
                           "launches": 5}), flush=True)
         return 0
-    log(f"generating config {args.config}")
-    w = configs.FULL[args.config](page_order=args.page_order)
-    log(w.summary())
-    pool = None
-    if args.layers > 1 or args.layout != "layer_first":
-        import paged_kv_attention_08_amd as pkv
-        layout = {"layer_first": pkv.KVCacheTensors.LAYER_FIRST, "page_first": pkv.KVCacheTensors.PAGE_FIRST,
-                  "row_interleaved": pkv.KVCacheTensors.ROW_INTERLEAVED}[args.layout]
-        cache = pkv.KVCacheTensors(args.layers, w.num_pool_rows, w.num_kv_heads, w.head_dim, w.page_size, layout)
-        pool = cache.layer(0)
-    ds = DeviceStep(w, pool=pool)
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda") if args.flush else None
-
-    has_decode = w.num_decode > 0
-    has_extend = w.num_decode < w.num_reqs
-
-    def step(marks):
-        """One pass of the path.  `marks` maps a position to an event recorded
-        there: 0..3 before metadata, store, decode and extend, 4 after the last
-        call."""
-        def mark(j):
-            e = marks.get(j)
-            if e is not None:
-                e.record(stream)
-        mark(0)
-        ds.metadata()
-        mark(1)
-        ds.store()
-        mark(2)
-        if has_decode:
-            ds.decode()
-        mark(3)
-        if has_extend:
-            ds.extend()
-        mark(4)
-
-    log(f"warmup {args.warmup} steps, then {args.settle_ms} ms of steps for the clocks to settle")
-    for _ in range(args.warmup):
-        step({})
-    torch.cuda.synchronize()
-    # Under a fresh load the GPU runs at lower clocks for its first ~100 ms
-    # (extend on the shared-prefix batch: 460 us per call over steps 5..25,
-    # 394 us after 200 steps); untimed steps until the clocks have settled.
-    settle_steps = 0
-    t_settle = time.perf_counter()
-    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
-        for _ in range(8):
-            step({})
-        torch.cuda.synchronize()
-        settle_steps += 8
-    assert ds.status() == 0, f"device status {ds.status():#x}"
-
-    # Per-call breakdown: an event before every call.  Each recorded event adds
-    # a few microseconds to the stream, so the step time comes from a second
-    # pass below with events around the dominant call only.
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    log(f"breakdown over {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        if flush_buf is not None:
-            flush_buf.fill_(float(k))
-        step({j: events[k][j] for j in range(5)})
-    torch.cuda.synchronize()
-    breakdown_wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    parts = np.array([[events[k][j].elapsed_time(events[k][j + 1]) for j in range(4)] for k in range(args.steps)])
-    mean_ms = parts.mean(axis=0)  # metadata, store, decode, extend
-    step_ms = float(parts.sum(axis=1).mean())
-    decode_dominant = has_decode and (not has_extend or mean_ms[2] >= mean_ms[3])
-
-    # Timed pass: K steps, events only around the dominant call (its launch
-    # duration for the roofline), wall clock for the step.
-    pos = (2, 3) if decode_dominant else (3, 4)
-    pairs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    log(f"timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        if flush_buf is not None:
-            flush_buf.fill_(float(k))
-        step({pos[0]: pairs[k][0], pos[1]: pairs[k][1]})
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    assert ds.status() == 0, f"device status {ds.status():#x}"
-    dominant_ms = float(np.mean([pairs[k][0].elapsed_time(pairs[k][1]) for k in range(args.steps)]))
-    dominant_in_breakdown_ms = float(mean_ms[2 if decode_dominant else 3])
-    mean_ms[2 if decode_dominant else 3] = dominant_ms
-    wall_ms = wall * 1e3 / args.steps
-    ms_per_step = step_ms if args.flush else wall_ms
-
-    real = ~w.is_padding
-    dec_mask = np.zeros(w.num_reqs, dtype=bool)
-    dec_mask[:w.num_decode] = True
-    dec_bytes = PM.decode_bytes(w.device_len[dec_mask & real], w.num_qo_heads, w.num_kv_heads, w.head_dim,
-                                w.page_size)
-    st_bytes = PM.store_bytes(int((w.device_len[real] - w.cached_len[real]).sum()), w.num_kv_heads, w.head_dim)
-    md_bytes = PM.metadata_bytes(w.num_reqs, w.num_tokens)
-    ext_flops = PM.extend_flops(w.cached_len[~dec_mask], w.device_len[~dec_mask], w.num_qo_heads, w.head_dim)
-
-    decode_gbps = dec_bytes / (mean_ms[2] * 1e-3) / 1e9 if has_decode else None
-    extend_tflops = ext_flops / (mean_ms[3] * 1e-3) / 1e12 if has_extend else None
-    store_gbps = st_bytes / (mean_ms[1] * 1e-3) / 1e9
-    from paged_kv_attention_08_amd import profiling
-    call = "paged_decode_attn" if decode_dominant else "paged_extend_attn"
-    measured = profiling.traffic_for(call, args.config)  # None unless taken on the current kernel sources
-    traffic = None if measured is None else round(measured["traffic_bytes"])
-    if decode_dominant:
-        value = (dec_bytes + st_bytes + md_bytes) / (ms_per_step * 1e-3) / 1e9
-        unit = "GB/s"
-        roof = {"bound": "hbm", "achieved": round(decode_gbps, 1), "peak": PM.HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(decode_gbps / PM.HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                "kernel": "paged_decode_attn (decode_kernel + decode_merge_kernel)",
-                "algorithmic_bytes_per_launch": dec_bytes, "avg_launch_ms": round(float(mean_ms[2]), 4),
-                "profile": None if measured is None else measured["summary"]}
+    cfgs = [args.config] if args.config else [int(x) for x in args.configs.split(",") if x.strip()]
+    flush_buf = None if args.no_flush else torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    results, roofs = {}, {}
+    for cfg in cfgs:
+        results[cfg], roofs[cfg] = measure(cfg, args, torch, flush_buf)
+        log(f"config {cfg}: " + json.dumps({k: v for k, v in results[cfg].items()
+                                             if k in ("step_ms", "calls_ms", "decode_frac_hbm", "extend_frac_mfma",
+                                                      "extend_unflushed_frac_mfma")}))
+    head = 2 if 2 in results else cfgs[0]
+    r = results[head]
+    if "step_gbps" in r:
+        value, unit = r["step_gbps"], "GB/s"
     else:
-        value = ext_flops / (ms_per_step * 1e-3) / 1e12
-        unit = "TFLOP/s"
-        roof = {"bound": "mfma", "achieved": round(extend_tflops, 1), "peak": PM.BF16_DENSE_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(extend_tflops / PM.BF16_DENSE_PEAK_TFLOPS, 4), "traffic": traffic,
-                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                "kernel": "paged_extend_attn (extend_kernel)", "algorithmic_flops_per_launch": ext_flops,
-                "avg_launch_ms": round(float(mean_ms[3]), 4),
-                "profile": None if measured is None else measured["summary"]}
-
+        value, unit = r["step_tflops"], "TFLOP/s"
+    timing = ("median of K steps, events on the launch stream, " +
+              ("L2 + MALL flushed (1 GiB read pass) before each step" if flush_buf is not None else "no flush"))
     out = {
-        "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "settle_steps": settle_steps, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": WORKLOAD_TEXT[args.config], "config_index": args.config,
-                   "global_batch": w.num_reqs, "new_tokens": w.num_tokens, "parallelism": "single GPU",
-                   "l2_mall_flush_between_steps": bool(args.flush), "page_order": args.page_order,
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": r["step_ms"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[head], "config_index": head, "parallelism": "single GPU",
+                   "timing": timing, "page_order": args.page_order,
                    "kv_cache": f"{args.layers} layer(s), {args.layout}, step on layer 0"},
-        "breakdown_ms": {"metadata": round(float(mean_ms[0]), 4), "kv_store": round(float(mean_ms[1]), 4),
-                         "decode": round(float(mean_ms[2]), 4), "extend": round(float(mean_ms[3]), 4),
-                         "wall_per_step": round(wall_ms, 4), "events_per_step": round(step_ms, 4),
-                         "wall_per_step_with_breakdown_events": round(breakdown_wall_ms, 4),
-                         "dominant_call_in_breakdown_pass": round(dominant_in_breakdown_ms, 4)},
-        "decode_gbps": None if decode_gbps is None else round(decode_gbps, 1),
-        "decode_frac_hbm": None if decode_gbps is None else round(decode_gbps / PM.HBM_PEAK_GBPS, 4),
-        "extend_tflops": None if extend_tflops is None else round(extend_tflops, 1),
-        "extend_frac_mfma": None if extend_tflops is None else round(extend_tflops / PM.BF16_DENSE_PEAK_TFLOPS, 4),
-        "store_gbps": round(store_gbps, 1),
-        "roofline": roof,
+        "roofline": roofs[head],
+        "cpu_baseline": r.get("cpu_baseline"),
     }
-    out["next_rows"] = {}
-    if has_decode and not has_extend:
-        out["next_rows"]["decode_graph"] = graph_measurement(ds, w, args, stream)
-    out["next_rows"]["page_alloc"] = alloc_measurement(ds, w, args, stream)
-    out["next_rows"]["kv_store_rope"] = rope_measurement(ds, w, args, stream, PM)
-    ds.free()
-    if not args.no_cpu_baseline:
-        log("cpu baseline (fp64 oracle)")
-        out["cpu_baseline"] = cpu_baseline(w, "decode" if decode_dominant else "extend", args.cpu_budget)
-    else:
-        out["cpu_baseline"] = None
+    ext_cfg = 3 if 3 in results else next((c for c in cfgs if "extend_frac_mfma" in results[c] and
+                                           roofs[c]["bound"] == "mfma"), None)
+    if ext_cfg is not None and ext_cfg != head:
+        e = results[ext_cfg]
+        out["extend"] = {"workload": WORKLOAD_TEXT[ext_cfg], "config_index": ext_cfg, "value": e["extend_tflops"],
+                         "unit": "TFLOP/s", "frac_mfma": e["extend_frac_mfma"], "ms": e["calls_ms"]["extend"],
+                         "unflushed_ms": e.get("extend_unflushed_ms"),
+                         "unflushed_frac_mfma": e.get("extend_unflushed_frac_mfma")}
+        out["roofline_extend"] = roofs[ext_cfg]
+        out["cpu_baseline_extend"] = e.get("cpu_baseline")
+    out["host"] = host_description()
+    out["workloads"] = {str(c): {k: v for k, v in results[c].items() if k != "workload"} for c in cfgs}
     print(json.dumps(out), flush=True)
     return 0
 

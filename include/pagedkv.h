@@ -54,6 +54,7 @@ extern "C" {
 #define PKV_ERR_UNSUPPORTED       2  /* head_dim != 128, Hq/Hkv outside 1..16, page_size not a power of two <= 64 */
 #define PKV_ERR_WORKSPACE         3  /* plan or workspace smaller than the size query returns */
 #define PKV_ERR_HIP               4  /* a kernel launch failed; see pkv_last_hip_error() */
+#define PKV_ERR_HOST_ALLOC        5  /* a host allocation failed (pkv_decode_graph_create only) */
 
 /* ---- device status bits (sticky; OR-ed into *status by kernels) ---------- */
 #define PKV_STATUS_BAD_OUT_LOC    0x01  /* out_loc[t] outside [0, num_rows): token skipped by kv_store */
@@ -374,28 +375,77 @@ typedef struct pkv_decode_graph pkv_decode_graph;  /* opaque, host side */
  * buffers' contents are not read during capture).  This is the one call that
  * allocates: host memory and the graphs' driver objects, no device memory,
  * released by pkv_decode_graph_destroy.  A failing host check of any of the
- * three calls is returned and nothing is kept. */
+ * three calls is returned and nothing is kept; PKV_ERR_HOST_ALLOC if the
+ * graph object cannot be allocated. */
 int pkv_decode_graph_create(const pkv_decode_graph_desc* desc, const int32_t* sizes, int32_t num_sizes,
                             pkv_decode_graph** graph, void* stream);
 
 /* pkv_decode_graph_replay: the caller has written its num_reqs real decode
  * requests into slots [0, num_reqs) of table_idx / cached_len / device_len /
- * q / k_new / v_new and their num_alloc new-page rows into alloc_rows[0,
- * num_alloc) (num_alloc <= num_reqs; with page_size 1 it equals num_reqs).
- * The call picks the smallest captured size bs >= num_reqs (written to
- * *graph_size if non-NULL), turns slots [num_reqs, bs) into dummy requests on
- * dummy_table_row (cached_len 0, device_len 1, new row 0 on the dummy page),
- * and launches that graph on stream.  Outputs of the real requests are in
- * o[0, num_reqs).  Replays on one graph object must not overlap. */
-int pkv_decode_graph_replay(pkv_decode_graph* graph, int32_t num_reqs, int32_t num_alloc, int32_t* graph_size,
-                            void* stream);
+ * q / k_new / v_new and their new-page rows into alloc_rows, request by
+ * request from entry 0 (one entry per page a request needs; with page_size 1
+ * exactly num_reqs entries).  The call picks the smallest captured size
+ * bs >= num_reqs (written to *graph_size if non-NULL) and launches that graph
+ * on stream, with num_reqs set in its first kernel: that kernel turns slots
+ * [num_reqs, bs) into dummy requests on dummy_table_row (cached_len 0,
+ * device_len 1, their one new row the dummy page's row 0, written to those
+ * slots of table_idx / cached_len / device_len) and counts the real
+ * requests' new pages on the device, so alloc_rows[num_reqs..] is not read.
+ * One launch per replay.  Outputs of the real requests are in o[0, num_reqs).
+ * Replays on one graph object must not overlap. */
+int pkv_decode_graph_replay(pkv_decode_graph* graph, int32_t num_reqs, int32_t* graph_size, void* stream);
 
 int pkv_decode_graph_destroy(pkv_decode_graph* graph);
+
+/* ---- plan inspection (diagnostics and tests) ------------------------------ */
+
+/* Where the plan that build_attn_metadata writes (for batches of at most
+ * max_reqs requests and max_tokens new tokens, these head counts) keeps the
+ * work lists the attention calls follow.  The plan stays opaque to the calls;
+ * this lets a caller copy it to the host and check that the work lists cover
+ * every (request, KV head, key) of the decode requests and every (request, new
+ * token) of the extend requests exactly once.  Offsets are bytes from the
+ * start of the plan.
+ *   header, int32[8]:
+ *     [0] decode tiles in the flat order (see below)
+ *     [1] decode tiles per run ("per")
+ *     [2] extend tiles listed
+ *     [3] new tokens per extend tile (extend_tile_tokens)
+ *     [4] decode runs that received tiles
+ *   decode_tile_ptr, int32[B+1]: running total of the decode tiles of each
+ *     request in one group's sequence: ceil(device_len / decode_tile_keys) for
+ *     a valid decode request, 0 for extend and invalid requests.
+ *   extend_tiles, int32 pairs [header[2]]: (request, first new-token offset);
+ *     a tile covers new tokens [offset, offset + extend_tile_tokens) of the
+ *     request (clipped to its extend_len), for every KV head.
+ * The decode split (flash-decoding over the keys, learning notes kernel
+ * passage): the flat order is request-major, then group of
+ * decode_group_heads consecutive KV heads, then 32-key tile; with
+ * Hg = Hkv / decode_group_heads groups, request i's group gg holds flat tiles
+ * Hg * decode_tile_ptr[i] + gg * n_i + [0, n_i), n_i its tile count, and flat
+ * tile kti of it covers keys [32 kti, min(32 kti + 32, device_len)) of the
+ * group's KV heads.  Run r (of decode_runs) takes flat tiles
+ * [r * per, min((r + 1) * per, header[0])).
+ * Returns PKV_ERR_INVALID_ARGUMENT / PKV_ERR_UNSUPPORTED as pkv_plan_bytes
+ * would return 0.  Host only. */
+typedef struct pkv_plan_view {
+  int64_t header_offset;
+  int64_t decode_tile_ptr_offset;
+  int64_t extend_tiles_offset;
+  int64_t total_bytes;           /* == pkv_plan_bytes(...) */
+  int32_t decode_runs;           /* runs the decode split spreads the flat order over */
+  int32_t decode_group_heads;    /* KV heads one run reads together */
+  int32_t decode_tile_keys;      /* keys per decode tile (32) */
+  int32_t extend_tile_tokens;    /* new tokens per extend tile */
+} pkv_plan_view;
+
+int pkv_plan_view_layout(int32_t max_reqs, int64_t max_tokens, int32_t num_qo_heads, int32_t num_kv_heads,
+                         pkv_plan_view* view);
 
 /* ---- diagnostics -------------------------------------------------------- */
 const char* pkv_error_string(int code);   /* static string, never NULL */
 int         pkv_last_hip_error(void);      /* hipError_t of the last PKV_ERR_HIP in this thread */
-int         pkv_version(void);             /* ABI version: 1 */
+int         pkv_version(void);             /* ABI version: 2 */
 
 #ifdef __cplusplus
 }

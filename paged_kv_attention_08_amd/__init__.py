@@ -23,7 +23,7 @@ from ._lib import (PKV_STATUS_BAD_ALLOC, PKV_STATUS_BAD_DECODE, PKV_STATUS_BAD_L
                    PKV_STATUS_FREE_OVERFLOW, PKV_STATUS_OUT_OF_PAGES, PKV_STATUS_TOKEN_COUNT)
 
 __all__ = ["PagedKVError", "KVPoolTensors", "KVCacheTensors", "BatchTensors", "MetadataBuffers", "kv_store", "build_attn_metadata",
-           "paged_decode_attn", "paged_extend_attn", "plan_bytes", "workspace_bytes", "library_path",
+           "paged_decode_attn", "paged_extend_attn", "plan_bytes", "workspace_bytes", "library_path", "plan_view",
            "rope_cos_sin_cache", "kv_store_rope", "PKV_STATUS_BAD_POSITION", "DecodeGraph", "PageFreeList",
            "PKV_STATUS_OUT_OF_PAGES", "PKV_STATUS_FREE_OVERFLOW",
            "PKV_STATUS_BAD_ALLOC", "PKV_STATUS_BAD_DECODE", "PKV_STATUS_BAD_LENGTHS", "PKV_STATUS_BAD_OUT_LOC",
@@ -194,6 +194,14 @@ def plan_bytes(max_reqs: int, max_tokens: int, num_qo_heads: int, num_kv_heads: 
     return n
 
 
+def plan_view(max_reqs: int, max_tokens: int, num_qo_heads: int, num_kv_heads: int) -> dict:
+    """Where the plan of such a batch keeps its work lists (pkv_plan_view_layout)."""
+    v = _lib.PlanView()
+    _check("pkv_plan_view_layout", _lib.lib().pkv_plan_view_layout(max_reqs, max_tokens, num_qo_heads,
+                                                                    num_kv_heads, ctypes.byref(v)))
+    return {name: getattr(v, name) for name, _ in _lib.PlanView._fields_}
+
+
 def workspace_bytes(max_reqs: int, num_qo_heads: int, head_dim: int = 128) -> int:
     n = _lib.lib().paged_attn_workspace_bytes(max_reqs, num_qo_heads, head_dim)
     if n == 0:
@@ -351,13 +359,14 @@ class DecodeGraph:
                                                   _stream(stream)))
         self._handle = handle
 
-    def replay(self, num_reqs: int, num_alloc: Optional[int] = None, stream=None) -> int:
+    def replay(self, num_reqs: int, stream=None) -> int:
         """Launch the graph for num_reqs real requests already written to the
-        buffers' first slots; returns the padded batch size used."""
+        buffers' first slots (their new-page rows from alloc_rows[0] on);
+        returns the padded batch size used."""
         bs = ctypes.c_int32(0)
         _check("pkv_decode_graph_replay",
-               _lib.lib().pkv_decode_graph_replay(self._handle, num_reqs, num_reqs if num_alloc is None else num_alloc,
-                                                  ctypes.byref(bs), _stream(stream or self._stream)))
+               _lib.lib().pkv_decode_graph_replay(self._handle, num_reqs, ctypes.byref(bs),
+                                                  _stream(stream or self._stream)))
         return bs.value
 
     def close(self) -> None:

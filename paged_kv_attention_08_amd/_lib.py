@@ -14,6 +14,7 @@ PKV_ERR_INVALID_ARGUMENT = 1
 PKV_ERR_UNSUPPORTED = 2
 PKV_ERR_WORKSPACE = 3
 PKV_ERR_HIP = 4
+PKV_ERR_HOST_ALLOC = 5
 
 PKV_STATUS_BAD_OUT_LOC = 0x01
 PKV_STATUS_BAD_LENGTHS = 0x02
@@ -74,6 +75,12 @@ class DecodeGraphDesc(ctypes.Structure):
                 ("workspace_bytes", c_size_t), ("reserved", c_int32)]
 
 
+class PlanView(ctypes.Structure):
+    _fields_ = [("header_offset", c_int64), ("decode_tile_ptr_offset", c_int64), ("extend_tiles_offset", c_int64),
+                ("total_bytes", c_int64), ("decode_runs", c_int32), ("decode_group_heads", c_int32),
+                ("decode_tile_keys", c_int32), ("extend_tile_tokens", c_int32)]
+
+
 # name -> (restype, argtypes); the exports of include/pagedkv.h
 PROTOTYPES = {
     "pkv_plan_bytes": (c_size_t, [c_int32, c_int64, c_int32, c_int32]),
@@ -94,7 +101,8 @@ PROTOTYPES = {
     "pkv_free_pages": (c_int, [POINTER(FreeList), c_void_p, c_int32, c_void_p, c_void_p]),
     "pkv_decode_graph_create": (c_int, [POINTER(DecodeGraphDesc), POINTER(c_int32), c_int32, POINTER(c_void_p),
                                         c_void_p]),
-    "pkv_decode_graph_replay": (c_int, [c_void_p, c_int32, c_int32, POINTER(c_int32), c_void_p]),
+    "pkv_decode_graph_replay": (c_int, [c_void_p, c_int32, POINTER(c_int32), c_void_p]),
+    "pkv_plan_view_layout": (c_int, [c_int32, c_int64, c_int32, c_int32, POINTER(PlanView)]),
     "pkv_decode_graph_destroy": (c_int, [c_void_p]),
     "pkv_error_string": (ctypes.c_char_p, [c_int]),
     "pkv_last_hip_error": (c_int, []),

@@ -120,6 +120,56 @@ size_t decode_ws_bytes(int32_t hq) {
 
 }  // namespace
 
+namespace pkv {
+
+int prepare_metadata(const pkv_batch* batch, const pkv_page_table* page_table, int32_t page_size,
+                     int64_t num_pool_rows, const int32_t* alloc_rows, int64_t num_alloc, int32_t num_qo_heads,
+                     int32_t num_kv_heads, const pkv_attn_metadata* meta, MetaArgs* out) {
+  int rc;
+  if ((rc = check_batch(batch)) != PKV_OK) return rc;
+  if ((rc = check_page_table(page_table)) != PKV_OK) return rc;
+  if (!pow2_le64(page_size)) return PKV_ERR_UNSUPPORTED;
+  if (num_pool_rows <= 0 || num_pool_rows >= (int64_t(1) << 31) || num_pool_rows % page_size != 0)
+    return PKV_ERR_INVALID_ARGUMENT;
+  if (num_alloc < 0 || (num_alloc > 0 && !alloc_rows)) return PKV_ERR_INVALID_ARGUMENT;
+  if ((rc = check_heads(num_qo_heads, num_kv_heads)) != PKV_OK) return rc;
+  PlanLayout L;
+  if ((rc = check_meta_common(meta, batch, num_qo_heads / num_kv_heads, num_kv_heads, &L)) != PKV_OK) return rc;
+  if (batch->num_tokens > 0 && (!meta->out_loc || !meta->positions)) return PKV_ERR_INVALID_ARGUMENT;
+  MetaArgs a{};
+  a.B = batch->num_reqs;
+  a.num_decode = batch->num_decode;
+  a.R = page_table->num_rows;
+  a.W = page_table->width;
+  a.page_shift = log2i(page_size);
+  a.group = num_qo_heads / num_kv_heads;
+  a.Hkv = num_kv_heads;
+  a.T = batch->num_tokens;
+  a.num_pool_rows = num_pool_rows;
+  a.num_alloc = num_alloc;
+  a.table_idx = batch->table_idx;
+  a.cached_len = batch->cached_len;
+  a.device_len = batch->device_len;
+  a.page_table = page_table->data;
+  a.alloc_rows = alloc_rows;
+  a.out_loc = meta->out_loc;
+  a.positions = meta->positions;
+  a.qo_indptr = meta->qo_indptr;
+  a.kv_indptr = meta->kv_indptr;
+  a.last_indices = meta->last_indices;
+  a.status = meta->status;
+  a.plan = static_cast<char*>(meta->plan);
+  a.layout = L;
+  a.fuse_tokens = 0;
+  a.pad_from = INT32_MAX;
+  a.dummy_row = 0;
+  a.pad_table_idx = a.pad_cached_len = a.pad_device_len = a.pad_alloc_rows = nullptr;
+  *out = a;
+  return PKV_OK;
+}
+
+}  // namespace pkv
+
 extern "C" {
 
 size_t pkv_plan_bytes(int32_t max_reqs, int64_t max_tokens, int32_t num_qo_heads, int32_t num_kv_heads) {
@@ -158,41 +208,10 @@ int build_attn_metadata(const pkv_batch* batch, const pkv_page_table* page_table
                         int64_t num_pool_rows, const int32_t* alloc_rows, int64_t num_alloc,
                         int32_t num_qo_heads, int32_t num_kv_heads, const pkv_attn_metadata* meta,
                         void* stream) {
-  int rc;
-  if ((rc = check_batch(batch)) != PKV_OK) return rc;
-  if ((rc = check_page_table(page_table)) != PKV_OK) return rc;
-  if (!pow2_le64(page_size)) return PKV_ERR_UNSUPPORTED;
-  if (num_pool_rows <= 0 || num_pool_rows >= (int64_t(1) << 31) || num_pool_rows % page_size != 0)
-    return PKV_ERR_INVALID_ARGUMENT;
-  if (num_alloc < 0 || (num_alloc > 0 && !alloc_rows)) return PKV_ERR_INVALID_ARGUMENT;
-  if ((rc = check_heads(num_qo_heads, num_kv_heads)) != PKV_OK) return rc;
-  PlanLayout L;
-  if ((rc = check_meta_common(meta, batch, num_qo_heads / num_kv_heads, num_kv_heads, &L)) != PKV_OK) return rc;
-  if (batch->num_tokens > 0 && (!meta->out_loc || !meta->positions)) return PKV_ERR_INVALID_ARGUMENT;
   MetaArgs a;
-  a.B = batch->num_reqs;
-  a.num_decode = batch->num_decode;
-  a.R = page_table->num_rows;
-  a.W = page_table->width;
-  a.page_shift = log2i(page_size);
-  a.group = num_qo_heads / num_kv_heads;
-  a.Hkv = num_kv_heads;
-  a.T = batch->num_tokens;
-  a.num_pool_rows = num_pool_rows;
-  a.num_alloc = num_alloc;
-  a.table_idx = batch->table_idx;
-  a.cached_len = batch->cached_len;
-  a.device_len = batch->device_len;
-  a.page_table = page_table->data;
-  a.alloc_rows = alloc_rows;
-  a.out_loc = meta->out_loc;
-  a.positions = meta->positions;
-  a.qo_indptr = meta->qo_indptr;
-  a.kv_indptr = meta->kv_indptr;
-  a.last_indices = meta->last_indices;
-  a.status = meta->status;
-  a.plan = static_cast<char*>(meta->plan);
-  a.layout = L;
+  const int rc = prepare_metadata(batch, page_table, page_size, num_pool_rows, alloc_rows, num_alloc, num_qo_heads,
+                                  num_kv_heads, meta, &a);
+  if (rc != PKV_OK) return rc;
   hipError_t e = launch_metadata(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : hip_failed(e);
 }
@@ -375,6 +394,24 @@ int kv_store_rope(const pkv_kv_pool* pool, void* q, int32_t num_qo_heads, const 
   return e == hipSuccess ? PKV_OK : hip_failed(e);
 }
 
+int pkv_plan_view_layout(int32_t max_reqs, int64_t max_tokens, int32_t num_qo_heads, int32_t num_kv_heads,
+                         pkv_plan_view* view) {
+  if (!view || max_reqs < 0 || max_tokens < 0) return PKV_ERR_INVALID_ARGUMENT;
+  const int rc = check_heads(num_qo_heads, num_kv_heads);
+  if (rc != PKV_OK) return rc;
+  const PlanLayout L = plan_layout(max_reqs, max_tokens, num_qo_heads / num_kv_heads, num_kv_heads);
+  const int32_t hg = decode_heads_per_group(num_kv_heads);
+  view->header_offset = 0;
+  view->decode_tile_ptr_offset = L.dec_tiles_off;
+  view->extend_tiles_offset = L.tiles_off;
+  view->total_bytes = L.total;
+  view->decode_runs = kDecodeWaves / hg;
+  view->decode_group_heads = hg;
+  view->decode_tile_keys = kDecodeTileKeys;
+  view->extend_tile_tokens = L.tile_q;
+  return PKV_OK;
+}
+
 const char* pkv_error_string(int code) {
   switch (code) {
     case PKV_OK: return "ok";
@@ -382,12 +419,13 @@ const char* pkv_error_string(int code) {
     case PKV_ERR_UNSUPPORTED: return "unsupported configuration";
     case PKV_ERR_WORKSPACE: return "plan or workspace too small";
     case PKV_ERR_HIP: return "HIP launch failure";
+    case PKV_ERR_HOST_ALLOC: return "host allocation failed";
     default: return "unknown error code";
   }
 }
 
 int pkv_last_hip_error(void) { return g_last_hip_error; }
 
-int pkv_version(void) { return 1; }
+int pkv_version(void) { return 2; }
 
 }  // extern "C"

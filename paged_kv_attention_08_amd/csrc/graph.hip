@@ -10,8 +10,9 @@
 // address it had during capture, and the attention plan re-made into fixed
 // buffers).  Here the plan is built on the GPU by build_attn_metadata inside
 // the graph, so a replay re-plans with no host work: the host only writes the
-// real requests into the fixed buffers, one small kernel turns the remaining
-// slots into dummy requests, and the graph is launched.
+// real requests into the fixed buffers and the number of real requests into
+// the graph's first kernel node (its argument block), and the graph's first
+// kernel turns the remaining slots into dummy requests before planning.
 #include <algorithm>
 #include <new>
 #include <vector>
@@ -23,34 +24,17 @@ struct pkv_decode_graph {
   std::vector<int32_t> sizes;          // ascending
   std::vector<hipGraph_t> graphs;
   std::vector<hipGraphExec_t> execs;
+  std::vector<hipGraphNode_t> plan_nodes;   // the metadata plan kernel of each graph (its only root)
+  std::vector<pkv::MetaArgs> plan_args;     // that node's argument block as captured
 };
-
-namespace pkv {
-namespace {
-
-// Slots [n_real, bs) become dummy requests: the all-zero page-table row, no
-// cached token, one new token whose row is the dummy page's first row.  Their
-// alloc entries (one page each) follow the real requests' entries.
-__global__ void __launch_bounds__(256) pad_kernel(int32_t* table_idx, int32_t* cached_len, int32_t* device_len,
-                                                  int32_t* alloc_rows, int32_t n_real, int32_t bs,
-                                                  int32_t n_alloc_real, int32_t dummy_row) {
-  const int k = blockIdx.x * blockDim.x + threadIdx.x;
-  if (n_real + k >= bs) return;
-  table_idx[n_real + k] = dummy_row;
-  cached_len[n_real + k] = 0;
-  device_len[n_real + k] = 1;
-  alloc_rows[n_alloc_real + k] = 0;
-}
-
-}  // namespace
-}  // namespace pkv
 
 using namespace pkv;
 
 namespace {
 
-// The step on a batch of bs decode requests, enqueued on s (captured by the caller).
-int enqueue_step(const pkv_decode_graph_desc& d, int32_t bs, hipStream_t s) {
+// The step on a batch of bs decode requests, enqueued on s (captured by the
+// caller).  *plan_args receives the metadata plan kernel's argument block.
+int enqueue_step(const pkv_decode_graph_desc& d, int32_t bs, MetaArgs* plan_args, hipStream_t s) {
   pkv_batch b;
   b.num_reqs = bs;
   b.num_decode = bs;
@@ -58,9 +42,20 @@ int enqueue_step(const pkv_decode_graph_desc& d, int32_t bs, hipStream_t s) {
   b.table_idx = d.table_idx;
   b.cached_len = d.cached_len;
   b.device_len = d.device_len;
-  int rc = build_attn_metadata(&b, &d.page_table, d.pool.page_size, d.pool.num_rows, d.alloc_rows, bs,
-                               d.num_qo_heads, d.pool.num_kv_heads, &d.meta, s);
+  MetaArgs a;
+  int rc = prepare_metadata(&b, &d.page_table, d.pool.page_size, d.pool.num_rows, d.alloc_rows, bs, d.num_qo_heads,
+                            d.pool.num_kv_heads, &d.meta, &a);
   if (rc != PKV_OK) return rc;
+  // padding: set per replay in the plan node's arguments (none at capture)
+  a.pad_from = bs;
+  a.dummy_row = d.dummy_table_row;
+  a.pad_table_idx = d.table_idx;
+  a.pad_cached_len = d.cached_len;
+  a.pad_device_len = d.device_len;
+  a.pad_alloc_rows = d.alloc_rows;
+  *plan_args = a;
+  hipError_t e = launch_metadata(a, s);
+  if (e != hipSuccess) return hip_failed(e);
   rc = kv_store(&d.pool, d.k_new, d.v_new, d.meta.out_loc, bs, d.meta.status, s);
   if (rc != PKV_OK) return rc;
   return paged_decode_attn(&d.pool, &d.page_table, &b, &d.meta, d.q, d.o, d.num_qo_heads, d.sm_scale, d.workspace,
@@ -73,6 +68,20 @@ void release(pkv_decode_graph* g) {
   for (hipGraph_t gr : g->graphs)
     if (gr) (void)hipGraphDestroy(gr);
   delete g;
+}
+
+// The graph's root: the metadata plan kernel, launched first in the capture.
+hipError_t find_plan_node(hipGraph_t graph, hipGraphNode_t* node) {
+  size_t n = 0;
+  hipError_t e = hipGraphGetRootNodes(graph, nullptr, &n);
+  if (e != hipSuccess) return e;
+  if (n != 1) return hipErrorInvalidValue;
+  e = hipGraphGetRootNodes(graph, node, &n);
+  if (e != hipSuccess) return e;
+  hipGraphNodeType type;
+  e = hipGraphNodeGetType(*node, &type);
+  if (e != hipSuccess) return e;
+  return type == hipGraphNodeTypeKernel ? hipSuccess : hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -93,20 +102,27 @@ int pkv_decode_graph_create(const pkv_decode_graph_desc* desc, const int32_t* si
   // the calls check everything else on the host during capture (a failed
   // check ends the capture and is returned)
   pkv_decode_graph* g = new (std::nothrow) pkv_decode_graph;
-  if (!g) return PKV_ERR_INVALID_ARGUMENT;
-  g->desc = d;
-  g->sizes.assign(sizes, sizes + num_sizes);
+  if (!g) return PKV_ERR_HOST_ALLOC;
+  try {
+    g->desc = d;
+    g->sizes.assign(sizes, sizes + num_sizes);
+    g->graphs.assign(num_sizes, nullptr);
+    g->execs.assign(num_sizes, nullptr);
+    g->plan_nodes.assign(num_sizes, nullptr);
+    g->plan_args.resize(num_sizes);
+  } catch (const std::bad_alloc&) {
+    delete g;
+    return PKV_ERR_HOST_ALLOC;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   // capture from the largest size down, as the pages describe
-  g->graphs.assign(num_sizes, nullptr);
-  g->execs.assign(num_sizes, nullptr);
   for (int32_t i = num_sizes - 1; i >= 0; --i) {
     hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
     if (e != hipSuccess) {
       release(g);
       return hip_failed(e);
     }
-    const int rc = enqueue_step(d, g->sizes[i], s);
+    const int rc = enqueue_step(d, g->sizes[i], &g->plan_args[i], s);
     hipGraph_t graph = nullptr;
     e = hipStreamEndCapture(s, &graph);
     if (rc != PKV_OK || e != hipSuccess) {
@@ -115,7 +131,8 @@ int pkv_decode_graph_create(const pkv_decode_graph_desc* desc, const int32_t* si
       return rc != PKV_OK ? rc : hip_failed(e);
     }
     g->graphs[i] = graph;
-    e = hipGraphInstantiate(&g->execs[i], graph, nullptr, nullptr, 0);
+    e = find_plan_node(graph, &g->plan_nodes[i]);
+    if (e == hipSuccess) e = hipGraphInstantiate(&g->execs[i], graph, nullptr, nullptr, 0);
     if (e != hipSuccess) {
       release(g);
       return hip_failed(e);
@@ -125,25 +142,24 @@ int pkv_decode_graph_create(const pkv_decode_graph_desc* desc, const int32_t* si
   return PKV_OK;
 }
 
-int pkv_decode_graph_replay(pkv_decode_graph* g, int32_t num_reqs, int32_t num_alloc, int32_t* graph_size,
-                            void* stream) {
-  if (!g || num_reqs <= 0 || num_alloc < 0 || num_alloc > num_reqs) return PKV_ERR_INVALID_ARGUMENT;
+int pkv_decode_graph_replay(pkv_decode_graph* g, int32_t num_reqs, int32_t* graph_size, void* stream) {
+  if (!g || num_reqs <= 0) return PKV_ERR_INVALID_ARGUMENT;
   auto it = std::lower_bound(g->sizes.begin(), g->sizes.end(), num_reqs);
   if (it == g->sizes.end()) return PKV_ERR_INVALID_ARGUMENT;  // larger than the largest captured size
   const size_t k = (size_t)(it - g->sizes.begin());
-  const int32_t bs = *it;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const pkv_decode_graph_desc& d = g->desc;
-  if (bs > num_reqs) {
-    const int32_t pad = bs - num_reqs;
-    hipLaunchKernelGGL(pad_kernel, dim3((unsigned)((pad + 255) / 256)), dim3(256), 0, s, d.table_idx, d.cached_len,
-                       d.device_len, d.alloc_rows, num_reqs, bs, num_alloc, d.dummy_table_row);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return hip_failed(e);
-  }
-  hipError_t e = hipGraphLaunch(g->execs[k], s);
+  // slots [num_reqs, bs) become dummy requests inside the graph's plan kernel
+  MetaArgs a = g->plan_args[k];
+  a.pad_from = num_reqs;
+  MetaArgs node_args;
+  void* argv[1];
+  hipKernelNodeParams p;
+  metadata_plan_node(a, &node_args, argv, &p);
+  hipError_t e = hipGraphExecKernelNodeSetParams(g->execs[k], g->plan_nodes[k], &p);
   if (e != hipSuccess) return hip_failed(e);
-  if (graph_size) *graph_size = bs;
+  e = hipGraphLaunch(g->execs[k], s);
+  if (e != hipSuccess) return hip_failed(e);
+  if (graph_size) *graph_size = *it;
   return PKV_OK;
 }
 

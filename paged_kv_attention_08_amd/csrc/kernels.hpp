@@ -78,6 +78,17 @@ struct MetaArgs {
   char* plan;
   PlanLayout layout;
   int32_t fuse_tokens;  // 1: plan_kernel also maps the tokens (small batches; see launch_metadata)
+  // Graph-replay padding: requests [pad_from, B) are dummy requests (table row
+  // dummy_row, cached_len 0, device_len 1, their new row the dummy page's row 0)
+  // whatever the batch arrays hold; plan_kernel writes those values (and the
+  // dummy page's row 0 as their alloc entry) into the arrays below for the
+  // later kernels.  pad_from = INT32_MAX: no padding.
+  int32_t pad_from;
+  int32_t dummy_row;
+  int32_t* pad_table_idx;
+  int32_t* pad_cached_len;
+  int32_t* pad_device_len;
+  int32_t* pad_alloc_rows;
 };
 
 struct AttnArgs {
@@ -114,6 +125,15 @@ hipError_t launch_free_pages(const AllocArgs& a, hipStream_t s);
 hipError_t launch_free_list_reset(int32_t* state, int32_t num_free, hipStream_t s);
 hipError_t launch_rope_cache(const RopeCacheArgs& a, hipStream_t s);
 hipError_t launch_metadata(const MetaArgs& a, hipStream_t s);
+// Host checks of build_attn_metadata's arguments and its kernel argument block
+// (no padding).  Returns a PKV_* code.
+int prepare_metadata(const pkv_batch* batch, const pkv_page_table* page_table, int32_t page_size,
+                     int64_t num_pool_rows, const int32_t* alloc_rows, int64_t num_alloc, int32_t num_qo_heads,
+                     int32_t num_kv_heads, const pkv_attn_metadata* meta, MetaArgs* a);
+// The plan kernel's launch as a graph kernel node: func, grid and block, and
+// kernelParams pointing at *args (which must outlive the use of *p); *args is
+// `a` as launch_metadata passes it.
+void metadata_plan_node(const MetaArgs& a, MetaArgs* args, void** argv, hipKernelNodeParams* p);
 hipError_t launch_decode(const AttnArgs& a, hipStream_t s);
 hipError_t launch_extend(const AttnArgs& a, hipStream_t s);
 

@@ -22,6 +22,11 @@
 // For a small batch (at most kFuseTokens new tokens and kFuseReqs requests)
 // plan_kernel maps the tokens itself, from an LDS copy of qo_indptr, and the
 // second launch and the gap before it are saved.
+// Inside a replayed decode graph the batch is padded here too (learning notes
+// graph passage: padding requests fill the batch up to the captured size and
+// point at the dummy page): requests from pad_from on are taken as dummy
+// requests whatever the arrays hold, and plan_kernel writes their values into
+// the arrays for the kernels that follow.
 // Integer work only; results are bit-exact by construction.
 #include "kernels.hpp"
 
@@ -42,14 +47,25 @@ struct ReqInfo {
   int32_t ext, dl, new_pages, dtiles, tiles;
 };
 
+// (table row, cached_len, device_len) of request i: a padding request from
+// pad_from on is a dummy request on the all-zero table row.
+struct ReqFields {
+  int32_t r, c, dl;
+};
+
+__device__ inline ReqFields req_fields(const MetaArgs& a, int i) {
+  if (i >= a.pad_from) return {a.dummy_row, 0, 1};
+  return {a.table_idx[i], a.cached_len[i], a.device_len[i]};
+}
+
 __device__ inline int32_t ceil_div_pow2(int32_t x, int32_t shift) {
   return (x + (1 << shift) - 1) >> shift;
 }
 
-__device__ inline bool request_ok(const MetaArgs& a, int i, int32_t* bits) {
-  const int32_t r = a.table_idx[i];
-  const int32_t c = a.cached_len[i];
-  const int32_t dl = a.device_len[i];
+__device__ inline bool request_ok(const MetaArgs& a, int i, const ReqFields& f, int32_t* bits) {
+  const int32_t r = f.r;
+  const int32_t c = f.c;
+  const int32_t dl = f.dl;
   bool ok = true;
   if (r < 0 || r >= a.R) { *bits |= PKV_STATUS_BAD_TABLE_IDX; ok = false; }
   if (c < 0 || c > dl || dl > a.W) { *bits |= PKV_STATUS_BAD_LENGTHS; ok = false; }
@@ -112,12 +128,13 @@ __device__ inline void map_token(const MetaArgs& a, int64_t t, const int32_t* qo
   }
   const int i = lo;
   int32_t bits = 0;
-  if (!request_ok(a, i, &bits)) {  // already reported by plan_kernel
+  const ReqFields f = req_fields(a, i);
+  if (!request_ok(a, i, f, &bits)) {  // already reported by plan_kernel
     unmapped();
     return;
   }
-  const int32_t r = a.table_idx[i];
-  const int32_t c = a.cached_len[i];
+  const int32_t r = f.r;
+  const int32_t c = f.c;
   const int32_t j = c + (int32_t)(t - qo[i]);
   const int32_t s = a.page_shift;
   const int32_t slot = j & ((1 << s) - 1);
@@ -129,6 +146,8 @@ __device__ inline void map_token(const MetaArgs& a, int64_t t, const int32_t* qo
     // the request's partially filled last cached page
     row = (int64_t)pt_row[j - slot] + slot;
     if (row < 0 || row >= a.num_pool_rows) bits |= PKV_STATUS_BAD_PAGE_ROW;
+  } else if (i >= a.pad_from) {
+    row = slot;  // a padding request's one new row: the dummy page
   } else {
     const int64_t ai = (int64_t)alloc_ptr[i] + (lp - first_new_page);
     if (ai >= a.num_alloc) {
@@ -182,9 +201,15 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(MetaArgs a) {
     const int i = base + tid;
     ReqInfo ri = {false, 0, 0, 0, 0, 0};  // valid, ext, dl, new_pages, dtiles, tiles
     if (i < a.B) {
-      const int32_t c = a.cached_len[i];
-      const int32_t dl = a.device_len[i];
-      ri.valid = request_ok(a, i, &bits);
+      const ReqFields f = req_fields(a, i);
+      if (i >= a.pad_from) {  // the later kernels read the padding from the arrays
+        a.pad_table_idx[i] = f.r;
+        a.pad_cached_len[i] = f.c;
+        a.pad_device_len[i] = f.dl;
+      }
+      const int32_t c = f.c;
+      const int32_t dl = f.dl;
+      ri.valid = request_ok(a, i, f, &bits);
       ri.ext = dl > c && c >= 0 ? dl - c : 0;
       ri.dl = dl > 0 ? dl : 0;
       ri.new_pages = (c >= 0 && c <= dl) ? ceil_div_pow2(dl, s) - ceil_div_pow2(c, s) : 0;
@@ -203,6 +228,9 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(MetaArgs a) {
       a.kv_indptr[i + 1] = carry[1] + ex[1] + ri.dl;
       a.last_indices[i] = qo_end - 1;
       alloc_ptr[i + 1] = carry[2] + ex[2] + ri.new_pages;
+      // a padding request's one new page is the dummy page (for token_kernel,
+      // which reads it from alloc_rows; the fused mapping below knows it)
+      if (i >= a.pad_from && carry[2] + ex[2] < a.num_alloc) a.pad_alloc_rows[carry[2] + ex[2]] = 0;
       dec_tile_ptr[i + 1] = carry[3] + ex[3] + ri.dtiles;
       const int32_t tb = carry[4] + ex[4];
       const int32_t cap_t = a.layout.cap_tiles;
@@ -241,8 +269,9 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(MetaArgs a) {
   const int32_t n_t = min(carry[4], a.layout.cap_tiles);  // the same in every thread
   if (n_t > 0) {  // decode-only batches skip the sort
     auto tile_bucket = [&](int2 t) -> int {
-      const int32_t ci = a.cached_len[t.x];
-      const int32_t di = a.device_len[t.x];
+      const ReqFields f = req_fields(a, t.x);
+      const int32_t ci = f.c;
+      const int32_t di = f.dl;
       const int32_t kv_end = min(di, ci + t.y + tq);
       return kSortBuckets - 1 - min(max(kv_end, 0) >> 6, kSortBuckets - 1);
     };
@@ -283,17 +312,33 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(MetaArgs a) {
   }
 }
 
+MetaArgs metadata_launch_args(const MetaArgs& a_in) {
+  MetaArgs a = a_in;
+  a.fuse_tokens = (a.T <= kFuseTokens && a.B <= kFuseReqs) ? 1 : 0;
+  return a;
+}
+
 }  // namespace
 
 hipError_t launch_metadata(const MetaArgs& a_in, hipStream_t s) {
-  MetaArgs a = a_in;
-  a.fuse_tokens = (a.T <= kFuseTokens && a.B <= kFuseReqs) ? 1 : 0;
+  const MetaArgs a = metadata_launch_args(a_in);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.T == 0 || a.fuse_tokens) return e;
   const int64_t blocks = (a.T + 255) / 256;
   hipLaunchKernelGGL(token_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+void metadata_plan_node(const MetaArgs& a, MetaArgs* args, void** argv, hipKernelNodeParams* p) {
+  *args = metadata_launch_args(a);
+  argv[0] = args;
+  p->func = reinterpret_cast<void*>(plan_kernel);
+  p->gridDim = dim3(1);
+  p->blockDim = dim3(kPlanThreads);
+  p->sharedMemBytes = 0;
+  p->kernelParams = argv;
+  p->extra = nullptr;
 }
 
 }  // namespace pkv

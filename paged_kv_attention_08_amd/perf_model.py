@@ -55,3 +55,23 @@ def rope_store_bytes(num_tokens: int, num_qo_heads: int, num_kv_heads: int, head
     q = 2 * t * num_qo_heads * head_dim * 2
     kv = 2 * t * num_kv_heads * head_dim * 2
     return q + 2 * kv + 8 * t + t * head_dim * 4 + (2 * head_dim * 2 if qk_norm else 0)
+
+
+def extend_unique_bytes(page_table, table_idx, cached_len, device_len, num_qo_heads: int, num_kv_heads: int,
+                        head_dim: int, page_size: int, dtype_bytes: int = 2) -> int:
+    """Bytes an extend pass must move at least once: every distinct K and V
+    row its requests see (a radix-shared prefix once; the batch's new rows
+    included), one page-table entry per visible key (per page at page size
+    > 1), and each new token's query and output rows.  page_table is the state
+    before the batch (cached entries only): new rows are distinct by
+    construction and counted by number."""
+    rows = set()
+    entries = 0
+    new = 0
+    for r, c, dl in zip(table_idx, cached_len, device_len):
+        c, dl = int(c), int(dl)
+        rows.update(np.asarray(page_table[int(r), :c], dtype=np.int64).tolist())
+        new += dl - c
+        entries += dl if page_size == 1 else -(-dl // page_size)
+    kv = (len(rows) + new) * 2 * num_kv_heads * head_dim * dtype_bytes
+    return int(kv + 4 * entries + new * 2 * num_qo_heads * head_dim * dtype_bytes)

@@ -3,6 +3,16 @@
 Bar (from the build's stated target): store, page table and metadata are
 bit-exact; bf16 attention outputs widened to fp64 are within max-abs 2e-2 and
 mean-abs 2e-3 of the unrounded fp64 oracle, over real (non-padding) tokens.
+
+Relative bounds on top of it.  With N(0,1) inputs a long context gives small
+outputs (|o| about 0.01-0.06 at 16K-32K keys), so the absolute bar alone
+cannot see a kernel that drops a 32-key tile or mis-merges a split piece (such
+a slip moves outputs by 2e-3 to 7e-3 there).  So the compared outputs must
+also satisfy max|d| / max|o_ref| <= 1e-2 and, for every (token, query head)
+row, max_e|d| / max_e|o_ref| <= 2e-2.  tests/test_parity_sensitivity.py shows
+on the CPU that the oracle's own output rounded to bf16 stays below a quarter
+of both, while the oracle with one 32-key tile dropped or counted twice
+exceeds both at the long-decode lengths.
 """
 from __future__ import annotations
 
@@ -13,6 +23,8 @@ from oracle.run import reference_step
 
 MAX_ABS_TOL = 2e-2
 MEAN_ABS_TOL = 2e-3
+REL_MAX_TOL = 1e-2   # max|d| / max|o_ref| over the compared outputs
+ROW_REL_TOL = 2e-2   # per (token, query head): max over dims of |d| / max over dims of |o_ref|
 
 
 def sample_tokens(w, per_request: int = 12, seed: int = 0):
@@ -69,6 +81,31 @@ def check_store(ds, ref, w, max_untouched: int = 20000, seed: int = 0):
     assert np.all(k == 0x7FC0) and np.all(v == 0x7FC0), "poison page written"
 
 
+def attention_error_stats(got: np.ndarray, want: np.ndarray) -> dict:
+    """Error figures of outputs got against the fp64 reference want, both
+    [tokens, Hq, d] (any leading shape whose last axis is the head dim)."""
+    diff = np.abs(got - want)
+    row_ref = np.abs(want).max(axis=-1)
+    row_err = diff.max(axis=-1)
+    return {"tokens": int(want.shape[0]), "max_abs": float(diff.max()), "mean_abs": float(diff.mean()),
+            "rel_max": float(diff.max() / max(np.abs(want).max(), 1e-30)),
+            "row_rel_max": float((row_err / np.maximum(row_ref, 1e-30)).max())}
+
+
+def bar_failures(stats: dict) -> list:
+    """The parts of the attention bar these figures miss (empty: within it)."""
+    out = []
+    if not stats["max_abs"] <= MAX_ABS_TOL:
+        out.append(f"max-abs {stats['max_abs']:.3e} > {MAX_ABS_TOL}")
+    if not stats["mean_abs"] <= MEAN_ABS_TOL:
+        out.append(f"mean-abs {stats['mean_abs']:.3e} > {MEAN_ABS_TOL}")
+    if not stats["rel_max"] <= REL_MAX_TOL:
+        out.append(f"max|d|/max|o| {stats['rel_max']:.3e} > {REL_MAX_TOL}")
+    if not stats["row_rel_max"] <= ROW_REL_TOL:
+        out.append(f"per-row max|d|/max|o| {stats['row_rel_max']:.3e} > {ROW_REL_TOL}")
+    return out
+
+
 def check_attention(ds, ref_out: dict, w, label: str = ""):
     toks = sorted(ref_out)
     if not toks:
@@ -76,12 +113,101 @@ def check_attention(ds, ref_out: dict, w, label: str = ""):
     got = ds.output_f64(toks)
     want = np.stack([ref_out[t] for t in toks])
     assert np.all(np.isfinite(got)), f"{label}: non-finite output"
-    diff = np.abs(got - want)
-    stats = {"tokens": len(toks), "max_abs": float(diff.max()), "mean_abs": float(diff.mean()),
-             "rel_max": float(diff.max() / max(np.abs(want).max(), 1e-30))}
-    assert stats["max_abs"] <= MAX_ABS_TOL, f"{label}: max-abs {stats['max_abs']:.3e} > {MAX_ABS_TOL}"
-    assert stats["mean_abs"] <= MEAN_ABS_TOL, f"{label}: mean-abs {stats['mean_abs']:.3e} > {MEAN_ABS_TOL}"
+    stats = attention_error_stats(got, want)
+    fails = bar_failures(stats)
+    assert not fails, f"{label}: " + "; ".join(fails)
     return stats
+
+
+def allowed_changed_rows(ref, w) -> np.ndarray:
+    """Pool rows the step may change: the rows of real new tokens (out_loc) and
+    the dummy page (padding writes land there)."""
+    allowed = np.zeros(w.num_pool_rows, dtype=bool)
+    real_tok = np.ones(w.num_tokens, dtype=bool)
+    starts = token_starts(w)
+    for i in np.nonzero(w.is_padding)[0]:
+        real_tok[starts[i]:starts[i + 1]] = False
+    rows = ref["meta"]["out_loc"][real_tok]
+    allowed[rows] = True
+    allowed[w.dummy_rows.start:w.dummy_rows.stop] = True
+    return allowed
+
+
+def changed_rows(before, after, chunk_rows: int = 1 << 16) -> np.ndarray:
+    """Rows whose bits differ between two device copies of a pool ([N, ...] int16)."""
+    n = before.shape[0]
+    out = torch.zeros(n, dtype=torch.bool, device=before.device)
+    for s0 in range(0, n, chunk_rows):
+        a = before[s0:s0 + chunk_rows].reshape(min(chunk_rows, n - s0), -1)
+        b = after[s0:s0 + chunk_rows].reshape(min(chunk_rows, n - s0), -1)
+        out[s0:s0 + chunk_rows] = (a != b).any(dim=1)
+    return out.cpu().numpy()
+
+
+def check_pool_unchanged_elsewhere(ds, before, allowed: np.ndarray):
+    """Every pool row outside `allowed` is bit-identical to the snapshot taken
+    before the step (kv_store writes nothing but out_loc rows and the dummy
+    page; attention writes no pool row)."""
+    after_k = ds.k_pool.view(torch.int16)
+    after_v = ds.v_pool.view(torch.int16)
+    ch = changed_rows(before[0], after_k) | changed_rows(before[1], after_v)
+    bad = np.nonzero(ch & ~allowed)[0]
+    assert bad.size == 0, f"{bad.size} pool rows outside out_loc and the dummy page changed, e.g. {bad[:8].tolist()}"
+    return int(ch.sum())
+
+
+def plan_arrays(plan: np.ndarray, view: dict, B: int):
+    hdr = plan[view["header_offset"]:view["header_offset"] + 32].view(np.int32)
+    off = view["decode_tile_ptr_offset"]
+    tptr = plan[off:off + 4 * (B + 1)].view(np.int32)
+    n_ext = int(hdr[2])
+    off = view["extend_tiles_offset"]
+    tiles = plan[off:off + 8 * n_ext].view(np.int32).reshape(n_ext, 2)
+    return hdr, tptr, tiles
+
+
+def check_plan_coverage(plan: np.ndarray, view: dict, w) -> dict:
+    """The plan's work lists, read back through the documented layout
+    (pkv_plan_view_layout), cover every (decode request, KV head, key) and every
+    (extend request, new token) exactly once; extend tiles come most keys first."""
+    B, nd, Hkv = w.num_reqs, w.num_decode, w.num_kv_heads
+    hdr, tptr, tiles = plan_arrays(plan, view, B)
+    total, per, n_ext, tq, runs_used = (int(x) for x in hdr[:5])
+    HG, runs, K = view["decode_group_heads"], view["decode_runs"], view["decode_tile_keys"]
+    Hg = Hkv // HG
+    dl = w.device_len.astype(np.int64)
+    cl = w.cached_len.astype(np.int64)
+    # decode: tile counts per request, then every key of every KV head once
+    want_n = np.where(np.arange(B) < nd, -(-dl // K), 0)
+    assert tptr[0] == 0 and np.array_equal(np.diff(tptr.astype(np.int64)), want_n), "decode tile offsets"
+    assert total == Hg * int(tptr[B]), "decode tile total"
+    if total:
+        assert 1 <= per and runs * per >= total and runs_used == -(-total // per), "decode run shares"
+        seg = Hg * tptr.astype(np.int64)
+        counts = {i: np.zeros((Hkv, int(dl[i])), dtype=np.int32) for i in range(nd)}
+        for r in range(runs):
+            for f in range(r * per, min((r + 1) * per, total)):
+                i = int(np.searchsorted(seg, f, side="right") - 1)
+                n = int(tptr[i + 1] - tptr[i])
+                local = f - int(seg[i])
+                gg, kti = divmod(local, n)
+                counts[i][gg * HG:(gg + 1) * HG, K * kti:min(K * kti + K, int(dl[i]))] += 1
+        for i, c in counts.items():
+            assert c.min() == 1 and c.max() == 1, f"decode request {i}: keys covered {c.min()}..{c.max()} times"
+    # extend: every new token of every extend request once
+    ext = dl - cl
+    cover = {i: np.zeros(int(ext[i]), dtype=np.int32) for i in range(nd, B)}
+    for i, t0 in tiles:
+        i, t0 = int(i), int(t0)
+        assert nd <= i < B and t0 % tq == 0 and 0 <= t0 < ext[i], f"extend tile ({i}, {t0})"
+        cover[i][t0:t0 + tq] += 1
+    for i, c in cover.items():
+        assert c.size == 0 or (c.min() == 1 and c.max() == 1), f"extend request {i}: tokens covered {c.min()}..{c.max()}"
+    if n_ext:
+        kv_end = np.minimum(dl[tiles[:, 0]], cl[tiles[:, 0]] + tiles[:, 1] + tq)
+        bucket = np.minimum(kv_end >> 6, 1023)
+        assert np.all(np.diff(bucket) <= 0), "extend tiles not ordered most keys first"
+    return {"decode_tiles": total, "per": per, "runs_used": runs_used, "extend_tiles": n_ext}
 
 
 def real_outputs_finite(ds, w):

@@ -30,7 +30,8 @@ def test_help_lists_the_contract_flags():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"], capture_output=True, text=True,
                        timeout=120)
     assert r.returncode == 0
-    for flag in ("--gpus", "--steps", "--warmup", "--settle-ms", "--config"):
+    for flag in ("--gpus", "--steps", "--warmup", "--settle-ms", "--config", "--configs", "--no-flush",
+                 "--cpu-budget"):
         assert flag in r.stdout
 
 
@@ -38,6 +39,13 @@ def test_help_lists_the_contract_flags():
 def test_cpu_baseline_record(cfg, kind, unit):
     w = configs.small(cfg)
     rec = bench.cpu_baseline(w, kind, budget_s=0.5)
-    assert rec["kind"] == "oracle" and rec["unit"] == unit and rec["cores"] == 1
+    assert rec["kind"] == "oracle" and rec["unit"] == unit and rec["cores"] == 1 and rec["blas_threads"] == 1
     assert rec["value"] > 0 and rec["seconds"] > 0
     assert isinstance(rec["sample"], str) and rec["sample"]
+
+
+def test_host_description():
+    h = bench.host_description()
+    assert h["usable_cores"] == len(os.sched_getaffinity(0)) >= 1
+    assert h["os_cpu_count"] == os.cpu_count()
+    assert h["cpu_model"] is None or isinstance(h["cpu_model"], str)

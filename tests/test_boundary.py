@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.pkv_version() == 1
+    assert lib.pkv_version() == 2
     for code in range(6):
         assert lib.pkv_error_string(code)
     assert lib.pkv_last_hip_error() == 0
@@ -53,6 +53,27 @@ def test_size_queries(lib):
     assert lib.pkv_plan_bytes(256, 256, 64, 2) == 0      # group 32 > 16
     assert lib.pkv_plan_bytes(-1, 0, 32, 8) == 0
     assert lib.pkv_plan_bytes(10, 100, 32, 8) <= lib.pkv_plan_bytes(20, 100, 32, 8)
+
+
+def test_plan_view_layout(lib):
+    """The plan's documented work-list offsets fit inside pkv_plan_bytes and do
+    not overlap, for a few batch shapes; bad head counts are rejected."""
+    for (B, T, hq, hkv) in [(256, 256, 32, 8), (68, 8256, 32, 8), (32, 32, 64, 8), (3, 40, 12, 3), (0, 0, 8, 8)]:
+        v = _lib.PlanView()
+        assert lib.pkv_plan_view_layout(B, T, hq, hkv, ctypes.byref(v)) == _lib.PKV_OK
+        assert v.total_bytes == lib.pkv_plan_bytes(B, T, hq, hkv)
+        assert v.header_offset == 0 and v.decode_tile_ptr_offset >= 32
+        assert v.extend_tiles_offset >= v.decode_tile_ptr_offset + 4 * (B + 1)
+        tiles_cap = -(-T // v.extend_tile_tokens) + B
+        assert v.extend_tiles_offset + 8 * tiles_cap <= v.total_bytes
+        assert v.decode_tile_keys == 32 and v.extend_tile_tokens == 256 // (hq // hkv)
+        assert v.decode_group_heads in (1, 2, 4, 8) and hkv % v.decode_group_heads == 0
+        assert v.decode_runs * v.decode_group_heads == 2048
+    v = _lib.PlanView()
+    assert lib.pkv_plan_view_layout(8, 8, 32, 7, ctypes.byref(v)) == _lib.PKV_ERR_INVALID_ARGUMENT
+    assert lib.pkv_plan_view_layout(8, 8, 64, 2, ctypes.byref(v)) == _lib.PKV_ERR_UNSUPPORTED
+    assert lib.pkv_plan_view_layout(-1, 8, 32, 8, ctypes.byref(v)) == _lib.PKV_ERR_INVALID_ARGUMENT
+    assert lib.pkv_plan_view_layout(8, 8, 32, 8, None) == _lib.PKV_ERR_INVALID_ARGUMENT
     assert lib.paged_attn_workspace_bytes(256, 32, 128) > 0
     assert lib.paged_attn_workspace_bytes(256, 32, 64) == 0
     assert lib.paged_attn_workspace_bytes(256, 0, 128) == 0
@@ -239,7 +260,7 @@ def test_decode_graph_rejects_before_capture(lib):
     assert lib.pkv_decode_graph_create(ctypes.byref(d), big, 3, ctypes.byref(h), FAKE) == _lib.PKV_ERR_INVALID_ARGUMENT
     assert lib.pkv_decode_graph_create(ctypes.byref(d), sizes, 3, ctypes.byref(h), None) == \
         _lib.PKV_ERR_INVALID_ARGUMENT                     # the default stream cannot be captured
-    assert lib.pkv_decode_graph_replay(None, 1, 1, None, FAKE) == _lib.PKV_ERR_INVALID_ARGUMENT
+    assert lib.pkv_decode_graph_replay(None, 1, None, FAKE) == _lib.PKV_ERR_INVALID_ARGUMENT
     assert lib.pkv_decode_graph_destroy(None) == _lib.PKV_ERR_INVALID_ARGUMENT
 
 

@@ -2,7 +2,11 @@
 the C ABI: every replay's real outputs are bit-identical to the same padded
 batch run eagerly through the three calls, and within the attention bar of
 the fp64 oracle; replays of several padded sizes are interleaved with eager
-work and repeated (graph nodes must give the same result on every replay)."""
+work and repeated (graph nodes must give the same result on every replay).
+Around every replay the whole pool is compared with a copy taken before it:
+only the real requests' new rows and the dummy page may change, also at page
+size 16, where the real requests need fewer new pages than there are requests
+and earlier, larger batches have left other rows in alloc_rows past them."""
 import numpy as np
 import pytest
 import torch
@@ -23,11 +27,11 @@ def device_step(w):
     return ds
 
 
-def decode_workload(seed, page_size):
+def decode_workload(seed, page_size, nreq=16, num_pool_rows=1 << 14):
     rng = np.random.default_rng(seed)
-    reqs = [RequestSpec(int(L), int(L) + 1) for L in rng.integers(40, 400, size=16)]
+    reqs = [RequestSpec(int(L), int(L) + 1) for L in rng.integers(40, 400, size=nreq)]
     return build_workload("graph_decode", seed, reqs, num_qo_heads=32, num_kv_heads=8, head_dim=128,
-                          page_size=page_size, num_pool_rows=1 << 14, num_decode=16)
+                          page_size=page_size, num_pool_rows=num_pool_rows, num_decode=nreq)
 
 
 def new_pages(w, n):
@@ -73,27 +77,43 @@ def eager_padded(ds, w, n, bs, stream):
     return ds.o[:n].clone()
 
 
-@pytest.mark.parametrize("page_size", [1, 16])
-def test_graph_replay_matches_eager_and_oracle(page_size):
-    w = decode_workload(41 + page_size, page_size)
-    log(f"decode graph page_size {page_size}: {w.summary()}")
+# (page size, captured sizes, requests, replayed batch sizes in order); the
+# 520-request graph maps its tokens in build_attn_metadata's second kernel
+CASES = {"page1": (1, SIZES, 16, (16, 5, 1, 8, 3, 16, 5)),
+         "page16": (16, SIZES, 16, (16, 5, 1, 8, 3, 16, 5)),
+         "page16_520": (16, [8, 520], 520, (520, 300, 7, 520, 301))}
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_graph_replay_matches_eager_and_oracle(case):
+    page_size, sizes, nreq, order = CASES[case]
+    w = decode_workload(41 + page_size + nreq, page_size, nreq, 1 << 14 if nreq <= 16 else 1 << 17)
+    log(f"decode graph {case}: {w.summary()}")
     ds = device_step(w)
     stream = torch.cuda.Stream()
     ref = P.oracle_for(w)
     graph = pkv.DecodeGraph(ds.pool, ds.page_table, ds.batch, ds.alloc_rows, ds.q, ds.o, ds.k_new, ds.v_new,
-                            ds.meta, ds.workspace, w.sm_scale, int(w.dummy_table_row), SIZES, stream)
+                            ds.meta, ds.workspace, w.sm_scale, int(w.dummy_table_row), sizes, stream)
     try:
-        for n in (16, 5, 1, 8, 3, 16, 5):
-            bs = next(s for s in SIZES if s >= n)
+        for n in order:
+            bs = next(s for s in sizes if s >= n)
             want = eager_padded(ds, w, n, bs, stream)
             ds.o.fill_(float("nan"))
             torch.cuda.synchronize()
+            allowed = np.zeros(w.num_pool_rows, dtype=bool)
+            allowed[ref["meta"]["out_loc"][:n]] = True
+            allowed[w.dummy_rows.start:w.dummy_rows.stop] = True
             for rep in range(3):
-                na = write_real(ds, w, n)
+                write_real(ds, w, n)
                 torch.cuda.synchronize()
-                got_bs = graph.replay(n, na, stream=stream)
+                before = ds.snapshot_pool()
+                got_bs = graph.replay(n, stream=stream)
                 stream.synchronize()
                 assert got_bs == bs
+                P.check_pool_unchanged_elsewhere(ds, before, allowed)
+                k, v = ds.pool_rows_bits(ref["meta"]["out_loc"][:n])
+                assert np.array_equal(k, w.k_new[:n]) and np.array_equal(v, w.v_new[:n]), "stored rows"
+                del before
                 got = ds.o[:n].clone()
                 assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"n={n} replay {rep} != eager"
                 # eager work on the default stream between replays

@@ -3,24 +3,34 @@
 Small variants of the five workloads are checked on every output; the
 full-size workloads (the sizes the benchmark times, in the same launch
 configuration) are checked bit-exactly on metadata and store and on sampled
-attention outputs.  Planted-spike cases pin the gather at specific positions
-(first row, last row, split and page boundaries), where a dropped or shifted
-key would otherwise hide in the small N(0,1) outputs of long contexts.
+attention outputs.  Every case also checks that no pool row outside the new
+tokens' rows and the dummy page changed (whole pool, wherever a copy of it
+fits next to it) and reads the plan back to check that its work lists cover
+every (request, KV head, key) of the decode and every (request, new token) of
+the extend exactly once.  Planted-spike cases pin the gather at specific
+positions (first row, last row, tile, page and decode-run boundaries), where a
+dropped or shifted key would otherwise hide in the small N(0,1) outputs of
+long contexts.
 """
 import numpy as np
 import pytest
 import torch
 
 from workloads import RequestSpec, build_workload, configs
+import paged_kv_attention_08_amd as pkv
 from tests.gpu_harness import DeviceStep, log
 from tests import parity_checks as P
 
 pytestmark = pytest.mark.gpu
 
 
+WHOLE_POOL_MAX_ROWS = 1 << 22  # a copy of pools up to 16 GiB (K + V) is taken for the diff
+
+
 def run_case(w, decode_requests=None, extend_tokens=None, label=""):
     log(f"case {label}: {w.summary()}")
     ds = DeviceStep(w)
+    before = ds.snapshot_pool() if w.num_pool_rows <= WHOLE_POOL_MAX_ROWS else None
     log("  device step")
     ds.run()
     torch.cuda.synchronize()
@@ -29,6 +39,14 @@ def run_case(w, decode_requests=None, extend_tokens=None, label=""):
     ref = P.oracle_for(w, decode_requests, extend_tokens)
     P.check_metadata(ds, ref, w)
     P.check_store(ds, ref, w)
+    if before is not None:
+        n_changed = P.check_pool_unchanged_elsewhere(ds, before, P.allowed_changed_rows(ref, w))
+        del before
+        torch.cuda.empty_cache()
+        log(f"  whole pool: {n_changed} rows changed, all new-token or dummy rows")
+    plan, view = ds.plan_host()
+    cover = P.check_plan_coverage(plan, view, w)
+    log(f"  plan coverage ok {cover}")
     P.real_outputs_finite(ds, w)
     stats = P.check_attention(ds, ref["out"], w, label)
     log(f"  ok {stats}")
@@ -56,69 +74,144 @@ def test_full_config(cfg):
     ds.free()
 
 
-def _plant(w, positions):
-    """Make key `positions[i]` of request i dominate every query of the
-    request and give it a one-hot V; returns the expected one-hot rows."""
+def _bf16(x: np.ndarray) -> np.ndarray:
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _plant(w, spikes, seed=17):
+    """For each request i, make every key position in spikes[i] dominate all
+    queries of the request with one score (every query is a vector u, every
+    planted K row is 4u in all KV heads) and give each planted key a one-hot V
+    at its own dimension.  A token that sees n of them must return 1/n at each
+    of their dimensions and about 0 elsewhere.  Returns {i: [(position, dim)]}."""
     d = w.head_dim
     row_of_cached = {int(r): n for n, r in enumerate(w.cached_rows)}
     starts = P.token_starts(w)
-    expect = {}
-    rng = np.random.default_rng(17)
-    for i, j in positions.items():
+    rng = np.random.default_rng(seed)
+    planted = {}
+    owner = {}  # a radix-shared cached row is planted only by the first request that reads it
+    for i in sorted(spikes):
+        for j in range(int(w.cached_len[i])):
+            owner.setdefault(int(w.page_table[w.table_idx[i], j]), i)
+    for i, positions in spikes.items():
+        c = int(w.cached_len[i])
+        positions = sorted(set(int(j) for j in positions
+                               if j >= c or owner[int(w.page_table[w.table_idx[i], j])] == i))
+        assert len(positions) <= d, "one dimension per planted key"
         t0, t1 = starts[i], starts[i + 1]
         c = int(w.cached_len[i])
         u = rng.normal(size=d).astype(np.float32)
-        ub = (np.frombuffer(u.tobytes(), dtype=np.uint32) + 0x7FFF + ((np.frombuffer(u.tobytes(), dtype=np.uint32) >> 16) & 1)) >> 16
-        ub = ub.astype(np.uint16)
-        w.q[t0:t1, :, :] = ub[None, None, :]
-        kb = (np.frombuffer((u * 4).astype(np.float32).tobytes(), dtype=np.uint32))
-        kb = ((kb + 0x7FFF + ((kb >> 16) & 1)) >> 16).astype(np.uint16)
-        onehot = np.zeros(d, dtype=np.uint16)
-        hot = (i * 7) % d
-        onehot[hot] = 0x3F80  # 1.0
-        if j < c:
-            n = row_of_cached[int(w.page_table[w.table_idx[i], j])]
-            w.k_cached[n, :, :] = kb[None, :]
-            w.v_cached[n, :, :] = onehot[None, :]
-        else:
-            t = t0 + (j - c)
-            w.k_new[t, :, :] = kb[None, :]
-            w.v_new[t, :, :] = onehot[None, :]
-        vec = np.zeros(d)
-        vec[hot] = 1.0
-        expect[i] = (vec, j)
-    return expect
+        w.q[t0:t1, :, :] = _bf16(u)[None, None, :]
+        kb = _bf16(u * 4)
+        dims = rng.permutation(d)[:len(positions)]
+        for j, hot in zip(positions, dims):
+            onehot = np.zeros(d, dtype=np.uint16)
+            onehot[hot] = 0x3F80  # 1.0
+            if j < c:
+                n = row_of_cached[int(w.page_table[w.table_idx[i], j])]
+                w.k_cached[n, :, :] = kb[None, :]
+                w.v_cached[n, :, :] = onehot[None, :]
+            else:
+                t = t0 + (j - c)
+                w.k_new[t, :, :] = kb[None, :]
+                w.v_new[t, :, :] = onehot[None, :]
+        planted[i] = list(zip(positions, (int(x) for x in dims)))
+    return planted
 
 
-@pytest.mark.parametrize("kind", ["decode", "extend", "page64"])
-def test_planted_spikes(kind):
+def _check_spikes(ds, w, planted):
+    """Every real token returns 1/n at the dimensions of the n planted keys it
+    sees (to a quarter of 1/n) and no more than that error elsewhere."""
+    starts = P.token_starts(w)
+    checked = 0
+    for i, keys in planted.items():
+        c = int(w.cached_len[i])
+        toks = list(range(starts[i], starts[i + 1]))
+        got_all = ds.output_f64(toks)
+        for k, t in enumerate(toks):
+            pos = c + (t - starts[i])
+            vis = [dim for j, dim in keys if j <= pos]
+            if not vis:
+                continue
+            want = np.zeros(w.head_dim)
+            want[vis] = 1.0 / len(vis)
+            err = np.abs(got_all[k] - want[None, :]).max()
+            assert err < 0.25 / len(vis), (f"request {i} token {t}: {len(vis)} planted keys visible, "
+                                           f"max err {err:.3e}")
+            checked += 1
+    return checked
+
+
+def _run_boundary_keys(w, view):
+    """Key positions where one decode run's share of the flat tile order ends
+    and the next begins, inside each decode request, with the share `per` the
+    plan derives from the lengths (run r takes flat tiles [r per, (r+1) per))."""
+    K, HG, runs = view["decode_tile_keys"], view["decode_group_heads"], view["decode_runs"]
+    Hg = w.num_kv_heads // HG
+    n = [-(-int(w.device_len[i]) // K) for i in range(w.num_decode)]
+    seg = np.concatenate([[0], np.cumsum(n)]) * Hg
+    total = int(seg[-1])
+    per = max(1, -(-total // runs))
+    out = {i: [] for i in range(w.num_decode)}
+    for f in range(per, total, per):
+        i = int(np.searchsorted(seg, f, side="right") - 1)
+        local = f - int(seg[i])
+        kti = local % n[i]
+        if kti:  # a boundary inside the request's keys (not at a segment start)
+            out[i] += [K * kti - 1, K * kti]
+    return out, per
+
+
+def _spike_case(kind):
     if kind == "decode":
         w = configs.serving_decode(seed=31, real=12, padded_to=16, lo=1500, hi=2600, num_pool_rows=1 << 16)
-        pos = [0, 1, 31, 32, 63, 64, 255, 256, 511, 512, 1023, None]
     elif kind == "extend":
         w = configs.extend_radix(seed=32, nreq=3, prefix=256, tail_hi=200, chunk=300, num_pool_rows=1 << 14)
-        pos = [0, 270, None]
-    else:
+    elif kind == "page64":
         w = configs.mixed_page64(seed=33, ndec=8, dec_lo=600, dec_hi=900, next_=2, pre_hi=300, new_tokens=130,
                                  num_pool_rows=64 * 128)
-        pos = [0, 63, 64, 127, 128, 511, 512, None, 64, 0]
-    positions = {}
-    real = [i for i in range(w.num_reqs) if not w.is_padding[i]]
-    for n, i in enumerate(real):
-        p = pos[n % len(pos)]
-        dl = int(w.device_len[i])
-        positions[i] = dl - 1 if p is None or p >= dl else p
-    expect = _plant(w, positions)
+    elif kind == "long_runs":
+        # the long-decode shape: 64 query / 8 KV heads, contexts 16K-32K; 16
+        # requests, so each one spans about 16 decode runs
+        w = configs.long_decode(seed=34, batch=16, num_pool_rows=1 << 19)
+    else:  # "page64_runs": page size 64 at the mixed batch's decode lengths (1K-8K) plus extend requests
+        w = configs.mixed_page64(seed=35, ndec=16, next_=2, new_tokens=160, num_pool_rows=1 << 18)
+    return w
+
+
+@pytest.mark.parametrize("kind", ["decode", "extend", "page64", "long_runs", "page64_runs"])
+def test_planted_spikes(kind):
+    w = _spike_case(kind)
+    view = pkv.plan_view(w.num_reqs, w.num_tokens, w.num_qo_heads, w.num_kv_heads)
+    bounds, per = _run_boundary_keys(w, view)
+    s = w.page_size
+    spikes = {}
+    for i in range(w.num_reqs):
+        if w.is_padding[i]:
+            continue
+        dl, c = int(w.device_len[i]), int(w.cached_len[i])
+        pos = {0, dl - 1, min(31, dl - 1), min(32, dl - 1), min(63, dl - 1), min(64, dl - 1)}
+        if s > 1:  # page boundaries near the middle
+            m = max(1, (dl // 2) // s) * s
+            pos |= {m - 1, min(m, dl - 1)}
+        if i >= w.num_decode:  # last cached and first new key of an extend request
+            pos |= {max(c - 1, 0), c}
+        pos |= set(bounds.get(i, []))
+        spikes[i] = sorted(pos)
+    planted = _plant(w, spikes)
     ds, ref, _ = run_case(w, label=f"spike-{kind}")
-    starts = P.token_starts(w)
-    for i, (vec, j) in expect.items():
-        c = int(w.cached_len[i])
-        for t in range(starts[i], starts[i + 1]):
-            if c + (t - starts[i]) < j:
-                continue  # the planted key is not visible to this token
-            got = ds.output_f64([t])[0]
-            err = np.abs(got - vec[None, :]).max()
-            assert err < 2e-2, f"request {i} token {t} planted key {j}: max err {err:.3e}"
+    plan, _ = ds.plan_host()
+    hdr, _, _ = P.plan_arrays(plan, view, w.num_reqs)
+    if w.num_decode:
+        assert int(hdr[1]) == per, "spikes were placed for another decode share"
+    else:
+        assert not any(bounds.values())
+    n_bounds = sum(len(b) for b in bounds.values()) // 2
+    checked = _check_spikes(ds, w, planted)
+    log(f"  {checked} tokens checked, {n_bounds} run boundaries inside requests")
+    if kind in ("long_runs", "page64_runs"):
+        assert n_bounds >= 8 * w.num_decode
     ds.free()
 
 
