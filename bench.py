@@ -131,38 +131,49 @@ def cpu_baseline(w, kind: str, budget_s: float):
 def graph_measurement(ds, w, args, stream):
     """The decode step (metadata, store, decode attention) replayed as one HIP
     graph captured for this batch size, against the same three calls issued
-    eagerly; per-step latency from events around K back-to-back steps."""
+    eagerly; per-step time from events around K back-to-back steps (host
+    launch cost included: what a graph saves).  Replays with one real-request
+    count throughout, and with a count that changes on every replay (the
+    graph's first kernel node then gets new arguments each time)."""
     import torch
     import paged_kv_attention_08_amd as pkv
 
     side = torch.cuda.Stream()
     torch.cuda.synchronize()
+    saved = [t.clone() for t in (ds.batch.table_idx, ds.batch.cached_len, ds.batch.device_len)]
     graph = pkv.DecodeGraph(ds.pool, ds.page_table, ds.batch, ds.alloc_rows, ds.q, ds.o, ds.k_new, ds.v_new,
                             ds.meta, ds.workspace, w.sm_scale, int(w.dummy_table_row), [w.num_reqs], side)
     try:
         def timed(fn):
-            for _ in range(args.warmup):
-                fn()
+            for k in range(args.warmup):
+                fn(k)
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
             side.synchronize()
             ev[0].record(side)
-            for _ in range(args.steps):
-                fn()
+            for k in range(args.steps):
+                fn(k)
             ev[1].record(side)
             torch.cuda.synchronize()
             return ev[0].elapsed_time(ev[1]) / args.steps
 
-        def eager():
+        def eager(k):
             ds.metadata(side)
             ds.store(side)
             ds.decode(side)
 
+        n = w.num_reqs
         eager_ms = timed(eager)
-        graph_ms = timed(lambda: graph.replay(w.num_reqs, stream=side))
+        graph_ms = timed(lambda k: graph.replay(n, stream=side))
+        graph_var_ms = timed(lambda k: graph.replay(n - (k & 1), stream=side)) if n > 1 else graph_ms
     finally:
         graph.close()
+        torch.cuda.synchronize()
+        for t, v in zip((ds.batch.table_idx, ds.batch.cached_len, ds.batch.device_len), saved):
+            t.copy_(v)  # padding written into the last slot by the changing-count replays
+        torch.cuda.synchronize()
     assert ds.status() == 0, f"device status {ds.status():#x}"
     return {"batch": w.num_reqs, "eager_step_ms": round(eager_ms, 4), "graph_step_ms": round(graph_ms, 4),
+            "graph_step_ms_count_changing": round(graph_var_ms, 4),
             "what": "build_attn_metadata + kv_store + paged_decode_attn, eager launches vs one graph replay"}
 
 

@@ -26,6 +26,7 @@ struct pkv_decode_graph {
   std::vector<hipGraphExec_t> execs;
   std::vector<hipGraphNode_t> plan_nodes;   // the metadata plan kernel of each graph (its only root)
   std::vector<pkv::MetaArgs> plan_args;     // that node's argument block as captured
+  std::vector<int32_t> plan_pad_from;       // the real-request count the node's arguments now hold
 };
 
 using namespace pkv;
@@ -110,6 +111,7 @@ int pkv_decode_graph_create(const pkv_decode_graph_desc* desc, const int32_t* si
     g->execs.assign(num_sizes, nullptr);
     g->plan_nodes.assign(num_sizes, nullptr);
     g->plan_args.resize(num_sizes);
+    g->plan_pad_from.assign(num_sizes, -1);
   } catch (const std::bad_alloc&) {
     delete g;
     return PKV_ERR_HOST_ALLOC;
@@ -148,15 +150,24 @@ int pkv_decode_graph_replay(pkv_decode_graph* g, int32_t num_reqs, int32_t* grap
   if (it == g->sizes.end()) return PKV_ERR_INVALID_ARGUMENT;  // larger than the largest captured size
   const size_t k = (size_t)(it - g->sizes.begin());
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // slots [num_reqs, bs) become dummy requests inside the graph's plan kernel
-  MetaArgs a = g->plan_args[k];
-  a.pad_from = num_reqs;
-  MetaArgs node_args;
-  void* argv[1];
-  hipKernelNodeParams p;
-  metadata_plan_node(a, &node_args, argv, &p);
-  hipError_t e = hipGraphExecKernelNodeSetParams(g->execs[k], g->plan_nodes[k], &p);
-  if (e != hipSuccess) return hip_failed(e);
+  // slots [num_reqs, bs) become dummy requests inside the graph's plan kernel;
+  // its arguments are rewritten only when the count differs from the one they
+  // hold (a decode loop mostly replays one size with one count)
+  hipError_t e = hipSuccess;
+  if (g->plan_pad_from[k] != num_reqs) {
+    MetaArgs a = g->plan_args[k];
+    a.pad_from = num_reqs;
+    MetaArgs node_args;
+    void* argv[1];
+    hipKernelNodeParams p;
+    metadata_plan_node(a, &node_args, argv, &p);
+    e = hipGraphExecKernelNodeSetParams(g->execs[k], g->plan_nodes[k], &p);
+    if (e != hipSuccess) {
+      g->plan_pad_from[k] = -1;
+      return hip_failed(e);
+    }
+    g->plan_pad_from[k] = num_reqs;
+  }
   e = hipGraphLaunch(g->execs[k], s);
   if (e != hipSuccess) return hip_failed(e);
   if (graph_size) *graph_size = *it;
