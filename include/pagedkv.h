@@ -55,6 +55,7 @@ extern "C" {
 #define PKV_ERR_WORKSPACE         3  /* plan or workspace smaller than the size query returns */
 #define PKV_ERR_HIP               4  /* a kernel launch failed; see pkv_last_hip_error() */
 #define PKV_ERR_HOST_ALLOC        5  /* a host allocation failed (pkv_decode_graph_create only) */
+#define PKV_ERR_SCRATCH           6  /* the call needs more than the library's static scratch holds */
 
 /* ---- device status bits (sticky; OR-ed into *status by kernels) ---------- */
 #define PKV_STATUS_BAD_OUT_LOC    0x01  /* out_loc[t] outside [0, num_rows): token skipped by kv_store */
@@ -214,6 +215,26 @@ int paged_decode_attn(const pkv_kv_pool* pool, const pkv_page_table* page_table,
 int paged_extend_attn(const pkv_kv_pool* pool, const pkv_page_table* page_table, const pkv_batch* batch,
                       const pkv_attn_metadata* meta, const void* q, void* o, int32_t num_qo_heads,
                       float sm_scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* paged_decode_attn_static: paged_decode_attn without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  The split-K
+ * partial states go to a static device array of PKV_STATIC_SCRATCH_BYTES bytes
+ * inside the library; the call allocates nothing (no hipMalloc / hipFree).
+ * Each GPU the library runs on holds its own copy of the array until the
+ * process ends; the first call on a device looks up its address there.
+ * Limit: the array holds the partial states of up to 8 query heads per KV head
+ * (Hq / Hkv <= 8); a larger group returns PKV_ERR_SCRATCH before anything is
+ * enqueued.  Every call on one GPU shares that GPU's array: calls that overlap
+ * on one GPU (other streams, other threads) race, so the caller serialises
+ * them (one stream, or events between streams).  The array needs no clearing
+ * between calls: every partial state the merge reads is written earlier in the
+ * same call.  Results are bit-identical to paged_decode_attn's on the same
+ * inputs. */
+#define PKV_STATIC_SCRATCH_BYTES 17039360  /* 2048 wavefronts x 2 pieces x 8 heads x (128 + 2) floats */
+int paged_decode_attn_static(const pkv_kv_pool* pool, const pkv_page_table* page_table, const pkv_batch* batch,
+                             const pkv_attn_metadata* meta, const void* q, void* o, int32_t num_qo_heads,
+                             float sm_scale, void* stream);
 
 /* ---- all layers' KV cache in one buffer ------------------------------------ */
 

@@ -23,7 +23,7 @@ from ._lib import (PKV_STATUS_BAD_ALLOC, PKV_STATUS_BAD_DECODE, PKV_STATUS_BAD_L
                    PKV_STATUS_FREE_OVERFLOW, PKV_STATUS_OUT_OF_PAGES, PKV_STATUS_TOKEN_COUNT)
 
 __all__ = ["PagedKVError", "KVPoolTensors", "KVCacheTensors", "BatchTensors", "MetadataBuffers", "kv_store", "build_attn_metadata",
-           "paged_decode_attn", "paged_extend_attn", "plan_bytes", "workspace_bytes", "library_path", "plan_view",
+           "paged_decode_attn", "paged_decode_attn_static", "paged_extend_attn", "plan_bytes", "workspace_bytes", "library_path", "plan_view",
            "rope_cos_sin_cache", "kv_store_rope", "PKV_STATUS_BAD_POSITION", "DecodeGraph", "PageFreeList",
            "PKV_STATUS_OUT_OF_PAGES", "PKV_STATUS_FREE_OVERFLOW",
            "PKV_STATUS_BAD_ALLOC", "PKV_STATUS_BAD_DECODE", "PKV_STATUS_BAD_LENGTHS", "PKV_STATUS_BAD_OUT_LOC",
@@ -261,6 +261,27 @@ def paged_decode_attn(pool: KVPoolTensors, page_table: torch.Tensor, batch: Batc
                       q: torch.Tensor, o: torch.Tensor, sm_scale: float, workspace: torch.Tensor,
                       stream=None) -> None:
     _attn("paged_decode_attn", pool, page_table, batch, meta, q, o, sm_scale, workspace, stream)
+
+
+def paged_decode_attn_static(pool: KVPoolTensors, page_table: torch.Tensor, batch: BatchTensors,
+                             meta: MetadataBuffers, q: torch.Tensor, o: torch.Tensor, sm_scale: float,
+                             stream=None) -> None:
+    """paged_decode_attn with the library's static device scratch as its
+    workspace: allocates nothing (no device memory, no tensors).  Needs at most
+    8 query heads per KV head; calls that overlap on one GPU race."""
+    p = pool.struct()
+    b = batch.struct()
+    _need(page_table, "page_table", torch.int32, 2)
+    _need(q, "q", torch.bfloat16, 3)
+    _need(o, "o", torch.bfloat16, 3)
+    if q.shape != o.shape or q.shape[0] < batch.num_tokens or q.shape[2] != pool.k.shape[2]:
+        raise ValueError("q / o shapes do not match the batch and pool")
+    pt = _lib.PageTable(page_table.data_ptr(), page_table.shape[0], page_table.shape[1])
+    m = meta.struct()
+    _check("paged_decode_attn_static",
+           _lib.lib().paged_decode_attn_static(ctypes.byref(p), ctypes.byref(pt), ctypes.byref(b), ctypes.byref(m),
+                                               q.data_ptr(), o.data_ptr(), q.shape[1], float(sm_scale),
+                                               _stream(stream)))
 
 
 def paged_extend_attn(pool: KVPoolTensors, page_table: torch.Tensor, batch: BatchTensors, meta: MetadataBuffers,

@@ -15,6 +15,8 @@ PKV_ERR_UNSUPPORTED = 2
 PKV_ERR_WORKSPACE = 3
 PKV_ERR_HIP = 4
 PKV_ERR_HOST_ALLOC = 5
+PKV_ERR_SCRATCH = 6
+PKV_STATIC_SCRATCH_BYTES = 17039360
 
 PKV_STATUS_BAD_OUT_LOC = 0x01
 PKV_STATUS_BAD_LENGTHS = 0x02
@@ -92,6 +94,8 @@ PROTOTYPES = {
                                   c_void_p, c_void_p, c_int32, c_float, c_void_p, c_size_t, c_void_p]),
     "paged_extend_attn": (c_int, [POINTER(KVPool), POINTER(PageTable), POINTER(Batch), POINTER(AttnMetadata),
                                   c_void_p, c_void_p, c_int32, c_float, c_void_p, c_size_t, c_void_p]),
+    "paged_decode_attn_static": (c_int, [POINTER(KVPool), POINTER(PageTable), POINTER(Batch), POINTER(AttnMetadata),
+                                         c_void_p, c_void_p, c_int32, c_float, c_void_p]),
     "pkv_kv_cache_layer": (c_int, [POINTER(KVCache), c_int32, POINTER(KVPool)]),
     "pkv_rope_cos_sin_cache": (c_int, [c_void_p, c_int32, c_int32, ctypes.c_double, c_void_p]),
     "kv_store_rope": (c_int, [POINTER(KVPool), c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int64,

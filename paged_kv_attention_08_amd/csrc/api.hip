@@ -1,10 +1,18 @@
 // extern "C" entry points: host-side argument checks, then launches on the
 // caller's stream.  Nothing here allocates, frees or synchronises.
 #include <cmath>
+#include <mutex>
 
 #include "kernels.hpp"
 
 using namespace pkv;
+
+// Workspace of paged_decode_attn_static: the split-K partial states of up to
+// 8 query heads per KV head, one copy per GPU for the life of the process.  In
+// host code its name is a host-side stand-in, not a device address: only the
+// per-device address that hipGetSymbolAddress returns is passed to kernels.
+static_assert(decode_ws_floats(8) * 4 == PKV_STATIC_SCRATCH_BYTES, "header states the scratch size");
+static __device__ __align__(256) float scratch[PKV_STATIC_SCRATCH_BYTES / 4];
 
 namespace pkv {
 
@@ -245,6 +253,54 @@ int paged_extend_attn(const pkv_kv_pool* pool, const pkv_page_table* page_table,
   return e == hipSuccess ? PKV_OK : hip_failed(e);
 }
 
+// ---- the no-allocation decode variant: a static device array as workspace --
+
+namespace {
+
+constexpr int kScratchMaxGroup = 8;
+constexpr int kScratchMaxDevices = 64;
+
+std::mutex g_scratch_mutex;
+float* g_scratch_ptr[kScratchMaxDevices] = {};
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+hipError_t scratch_on_current_device(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = static_cast<float*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+int paged_decode_attn_static(const pkv_kv_pool* pool, const pkv_page_table* page_table, const pkv_batch* batch,
+                             const pkv_attn_metadata* meta, const void* q, void* o, int32_t num_qo_heads,
+                             float sm_scale, void* stream) {
+  AttnArgs a;
+  int rc = fill_attn_args(pool, page_table, batch, meta, q, o, num_qo_heads, sm_scale, &a);
+  if (rc != PKV_OK) return rc;
+  if (a.group > kScratchMaxGroup) return PKV_ERR_SCRATCH;
+  if (batch->num_decode == 0) return PKV_OK;
+  float* ws = nullptr;
+  hipError_t e = scratch_on_current_device(&ws);
+  if (e != hipSuccess) return hip_failed(e);
+  a.ws_acc = ws;
+  a.ws_ml = ws + (int64_t)kDecodeWaves * 2 * a.group * kHeadDim;
+  e = launch_decode(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : hip_failed(e);
+}
+
 namespace {
 
 int check_free_list(const pkv_free_list* f) {
@@ -420,6 +476,7 @@ const char* pkv_error_string(int code) {
     case PKV_ERR_WORKSPACE: return "plan or workspace too small";
     case PKV_ERR_HIP: return "HIP launch failure";
     case PKV_ERR_HOST_ALLOC: return "host allocation failed";
+    case PKV_ERR_SCRATCH: return "needs more than the static scratch holds";
     default: return "unknown error code";
   }
 }

@@ -73,7 +73,7 @@ __host__ __device__ inline int32_t decode_heads_per_group(int32_t num_kv_heads) 
 // partial states (the piece of the segment the run starts inside and of the
 // one it ends inside), each G query heads x
 // (head_dim fp32 accumulator + running max + running sum).
-__host__ __device__ inline int64_t decode_ws_floats(int32_t max_group) {
+__host__ __device__ constexpr int64_t decode_ws_floats(int32_t max_group) {
   return (int64_t)kDecodeWaves * 2 * max_group * (kHeadDim + 2);
 }
 

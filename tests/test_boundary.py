@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_strings(lib):
     assert lib.pkv_version() == 2
-    for code in range(6):
+    for code in range(7):
         assert lib.pkv_error_string(code)
     assert lib.pkv_last_hip_error() == 0
 
@@ -189,6 +189,32 @@ def test_decode_rejects_small_workspace(lib):
                                  need - 16, None) == _lib.PKV_ERR_WORKSPACE
     assert lib.paged_decode_attn(B(pool()), B(table()), B(batch()), B(meta()), FAKE, FAKE, 32, 0.088, None,
                                  need, None) == _lib.PKV_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(p=pool(head_dim=256)), _lib.PKV_ERR_UNSUPPORTED),
+    (dict(hq=12), _lib.PKV_ERR_INVALID_ARGUMENT),
+    (dict(hq=8 * 17), _lib.PKV_ERR_UNSUPPORTED),
+    (dict(hq=8 * 9), _lib.PKV_ERR_SCRATCH),     # 9 query heads per KV head: beyond the static scratch
+    (dict(hq=8 * 16), _lib.PKV_ERR_SCRATCH),
+    (dict(scale=0.0), _lib.PKV_ERR_INVALID_ARGUMENT),
+    (dict(q=None), _lib.PKV_ERR_INVALID_ARGUMENT),
+    (dict(m=meta(plan_bytes=8)), _lib.PKV_ERR_WORKSPACE),
+])
+def test_static_decode_rejects(lib, kw, code):
+    """The no-allocation decode variant checks like paged_decode_attn and
+    refuses groups its static scratch cannot hold, all before touching a device."""
+    p = kw.get("p", pool())
+    m = kw.get("m", meta())
+    assert lib.paged_decode_attn_static(B(p), B(table()), B(batch()), B(m), kw.get("q", FAKE), FAKE,
+                                        kw.get("hq", 32), kw.get("scale", 0.088), None) == code
+
+
+def test_static_scratch_size_is_the_stated_one(lib):
+    # 2048 wavefronts x 2 pieces x 8 heads x (128 + 2) floats, the workspace of an 8-head group
+    assert _lib.PKV_STATIC_SCRATCH_BYTES == 2048 * 2 * 8 * 130 * 4
+    assert lib.paged_attn_workspace_bytes(1, 8, 128) == _lib.PKV_STATIC_SCRATCH_BYTES
+    assert lib.paged_attn_workspace_bytes(1, 16, 128) > _lib.PKV_STATIC_SCRATCH_BYTES
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
