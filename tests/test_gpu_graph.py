@@ -141,3 +141,41 @@ def test_graph_rejects_batches_beyond_the_largest_size():
     finally:
         graph.close()
         ds.free()
+
+
+def test_back_to_back_replays_with_changing_counts():
+    """Replays enqueued without a wait between them, the second with one real
+    request fewer (the plan node's arguments are rewritten between the two
+    launches): each runs with its own count.  The new row of the request that
+    only the first replay treats as real must hold its K/V afterwards, and the
+    outputs are the second replay's, bit-identical to the eager padded batch."""
+    w = decode_workload(91, 1)
+    log(f"back-to-back replays: {w.summary()}")
+    ds = device_step(w)
+    stream = torch.cuda.Stream()
+    ref = P.oracle_for(w)
+    rows = ref["meta"]["out_loc"]
+    n = w.num_reqs
+    graph = pkv.DecodeGraph(ds.pool, ds.page_table, ds.batch, ds.alloc_rows, ds.q, ds.o, ds.k_new, ds.v_new,
+                            ds.meta, ds.workspace, w.sm_scale, int(w.dummy_table_row), [n], stream)
+    try:
+        want = eager_padded(ds, w, n - 1, n, stream)
+        for rep in range(5):
+            write_real(ds, w, n)
+            last = torch.as_tensor([int(rows[n - 1])], device=ds.device)
+            ds.k_pool[last] = 0
+            ds.v_pool[last] = 0
+            ds.o.fill_(float("nan"))
+            torch.cuda.synchronize()
+            graph.replay(n, stream=stream)
+            graph.replay(n - 1, stream=stream)
+            stream.synchronize()
+            k, v = ds.pool_rows_bits([int(rows[n - 1])])
+            assert np.array_equal(k[0], w.k_new[n - 1]) and np.array_equal(v[0], w.v_new[n - 1]), \
+                f"rep {rep}: the first replay did not run with all {n} requests"
+            got = ds.o[:n - 1]
+            assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"rep {rep}: outputs"
+            assert ds.status() == 0
+    finally:
+        graph.close()
+        ds.free()
