@@ -69,8 +69,31 @@ def _pick(table: dict, key: str) -> float:
     return vals[0]
 
 
+def algorithmic_bytes(call: str, config: int) -> int:
+    """Bytes one launch of `call` must move on workload `config` (perf_model):
+    decode K/V rows, page-table entries, q and o of the real decode requests;
+    extend q, o, every distinct K/V row it sees (new rows included) and its
+    page-table entries; store new rows in and out."""
+    import numpy as np
+    from workloads import configs
+    from . import perf_model as PM
+    w = configs.FULL[config]()
+    dec = np.zeros(w.num_reqs, dtype=bool)
+    dec[:w.num_decode] = True
+    real = ~w.is_padding
+    if call == "paged_decode_attn":
+        return PM.decode_bytes(w.device_len[dec & real], w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size)
+    if call == "paged_extend_attn":
+        m = ~dec
+        return PM.extend_unique_bytes(w.page_table, w.table_idx[m], w.cached_len[m], w.device_len[m],
+                                      w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size)
+    return PM.store_bytes(int((w.device_len[real] - w.cached_len[real]).sum()), w.num_kv_heads, w.head_dim)
+
+
 def summarize(args) -> dict:
     kernels = args.kernels.split(",")
+    if args.algorithmic_bytes is None:
+        args.algorithmic_bytes = float(algorithmic_bytes(args.call, args.config))
     stats = kernel_stats(args.trace)
     fetch = counter_means(args.fetch, "FETCH_SIZE")
     write = counter_means(args.write, "WRITE_SIZE")
@@ -83,7 +106,7 @@ def summarize(args) -> dict:
     total_ns = 0.0
     for name, calls, avg, pct in stats:
         short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
-        if any(k in name for k in kernels) or "pkv::" in name:
+        if any(k in name for k in kernels) or "pkv::" in name or "reduce" in name.lower():
             lines.append(f"| {short} | {calls} | {avg / 1e3:.2f} | {pct:.2f} |")
         if any(k in name for k in kernels):
             total_ns += avg
@@ -157,7 +180,8 @@ def main(argv=None):
     s.add_argument("--copy-fetch", required=True)
     s.add_argument("--copy-write", required=True)
     s.add_argument("--copy-kernel", default="copyBuffer")
-    s.add_argument("--algorithmic-bytes", type=float, default=0.0)
+    s.add_argument("--algorithmic-bytes", type=float, default=None,
+                   help="default: computed for --call on workload --config")
     s.add_argument("--command", required=True)
     s.add_argument("--extra", action="append", help="directory of another counter pass to list")
     s.add_argument("--out", required=True)
