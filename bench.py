@@ -144,21 +144,28 @@ def graph_measurement(ds, w, args, stream):
     graph = pkv.DecodeGraph(ds.pool, ds.page_table, ds.batch, ds.alloc_rows, ds.q, ds.o, ds.k_new, ds.v_new,
                             ds.meta, ds.workspace, w.sm_scale, int(w.dummy_table_row), [w.num_reqs], side)
     try:
+        # at least 200 back-to-back steps after 20 untimed ones: with 20 steps
+        # the first replays after the host-bound eager pass skewed the figure
+        steps = max(args.steps, 200)
+
         def timed(fn):
-            for k in range(args.warmup):
+            for k in range(max(args.warmup, 20)):
                 fn(k)
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
             side.synchronize()
             ev[0].record(side)
-            for k in range(args.steps):
+            for k in range(steps):
                 fn(k)
             ev[1].record(side)
             torch.cuda.synchronize()
-            return ev[0].elapsed_time(ev[1]) / args.steps
+            return ev[0].elapsed_time(ev[1]) / steps
 
         def eager(k):
-            ds.metadata(side)
-            ds.store(side)
+            if args.separate_store:
+                ds.metadata(side)
+                ds.store(side)
+            else:
+                ds.metadata_store(side)
             ds.decode(side)
 
         n = w.num_reqs
@@ -174,7 +181,7 @@ def graph_measurement(ds, w, args, stream):
     assert ds.status() == 0, f"device status {ds.status():#x}"
     return {"batch": w.num_reqs, "eager_step_ms": round(eager_ms, 4), "graph_step_ms": round(graph_ms, 4),
             "graph_step_ms_count_changing": round(graph_var_ms, 4),
-            "what": "build_attn_metadata + kv_store + paged_decode_attn, eager launches vs one graph replay"}
+            "what": "metadata + store + paged_decode_attn, eager calls vs one graph replay"}
 
 
 def alloc_measurement(ds, w, args, stream):
@@ -276,24 +283,29 @@ def measure(cfg, args, torch, flush_buf):
     has_decode = w.num_decode > 0
     has_extend = w.num_decode < w.num_reqs
 
+    # the calls of one step, in order; a batch of at most 512 new tokens does
+    # metadata and store in one launch (build_attn_metadata_store)
+    if args.separate_store:
+        calls = [("metadata", ds.metadata), ("kv_store", ds.store)]
+    else:
+        calls = [("metadata_and_store", ds.metadata_store)]
+    if has_decode:
+        calls.append(("decode", ds.decode))
+    if has_extend:
+        calls.append(("extend", ds.extend))
+    names = [n for n, _ in calls]
+
     def step(marks):
-        """One pass of the path; marks maps a position (0..3 before metadata,
-        store, decode and extend, 4 after the last call) to an event."""
-        def mark(j):
+        """One pass of the path; marks maps a position (j before call j, len(calls)
+        after the last) to an event."""
+        for j, (_, fn) in enumerate(calls):
             e = marks.get(j)
             if e is not None:
                 e.record(stream)
-        mark(0)
-        ds.metadata()
-        mark(1)
-        ds.store()
-        mark(2)
-        if has_decode:
-            ds.decode()
-        mark(3)
-        if has_extend:
-            ds.extend()
-        mark(4)
+            fn()
+        e = marks.get(len(calls))
+        if e is not None:
+            e.record(stream)
 
     def flush():
         if flush_buf is not None:
@@ -327,12 +339,13 @@ def measure(cfg, args, torch, flush_buf):
                          for k in range(args.steps)])
 
     flushed = flush_buf is not None
-    step_ms = float(np.median(timed_pass([0, 4], flushed)[:, 0]))
-    parts = np.median(timed_pass([0, 1, 2, 3, 4], flushed), axis=0)  # metadata, store, decode, extend
-    decode_dominant = has_decode and (not has_extend or parts[2] >= parts[3])
-    dom = (2, 3) if decode_dominant else (3, 4)
-    dom_ms = float(np.median(timed_pass(list(dom), flushed)[:, 0]))
-    unflushed_ms = float(np.median(timed_pass(list(dom), False)[:, 0])) if flushed else dom_ms
+    nc = len(calls)
+    step_ms = float(np.median(timed_pass([0, nc], flushed)[:, 0]))
+    parts = dict(zip(names, np.median(timed_pass(list(range(nc + 1)), flushed), axis=0)))
+    decode_dominant = has_decode and (not has_extend or parts["decode"] >= parts["extend"])
+    jd = names.index("decode" if decode_dominant else "extend")
+    dom_ms = float(np.median(timed_pass([jd, jd + 1], flushed)[:, 0]))
+    unflushed_ms = float(np.median(timed_pass([jd, jd + 1], False)[:, 0])) if flushed else dom_ms
     assert ds.status() == 0, f"device status {ds.status():#x}"
 
     real = ~w.is_padding
@@ -347,13 +360,11 @@ def measure(cfg, args, torch, flush_buf):
     measured = profiling.traffic_for(call, cfg)  # None unless taken on the current kernel sources
     traffic = None if measured is None else round(measured["traffic_bytes"])
     profile = None if measured is None else measured["summary"]
-    decode_ms = dom_ms if decode_dominant else float(parts[2])
-    extend_ms = dom_ms if not decode_dominant else float(parts[3])
+    decode_ms = dom_ms if decode_dominant else float(parts.get("decode", 0.0))
+    extend_ms = dom_ms if not decode_dominant else float(parts.get("extend", 0.0))
+    parts["decode" if decode_dominant else "extend"] = dom_ms
     out = {"workload": WORKLOAD_TEXT[cfg], "step_ms": round(step_ms, 4),
-           "calls_ms": {"metadata": round(float(parts[0]), 4), "kv_store": round(float(parts[1]), 4),
-                        "decode": round(decode_ms, 4) if has_decode else None,
-                        "extend": round(extend_ms, 4) if has_extend else None},
-           "settle_steps": settle}
+           "calls_ms": {n: round(float(v), 4) for n, v in parts.items()}, "settle_steps": settle}
     if has_decode:
         gbps = dec_bytes / (decode_ms * 1e-3) / 1e9
         out["decode_gbps"] = round(gbps, 1)
@@ -368,7 +379,8 @@ def measure(cfg, args, torch, flush_buf):
             out["extend_unflushed_frac_mfma"] = round(tfu / PM.BF16_DENSE_PEAK_TFLOPS, 4)
     else:
         out["decode_unflushed_ms"] = round(unflushed_ms, 4)
-    out["store_gbps"] = round(st_bytes / (float(parts[1]) * 1e-3) / 1e9, 1)
+    if "kv_store" in parts:
+        out["store_gbps"] = round(st_bytes / (float(parts["kv_store"]) * 1e-3) / 1e9, 1)
     if decode_dominant:
         roof = {"bound": "hbm", "achieved": out["decode_gbps"], "peak": PM.HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": out["decode_frac_hbm"], "traffic": traffic, "kernel": "decode_kernel + decode_merge_kernel",
@@ -412,6 +424,8 @@ def main(argv=None):
     ap.add_argument("--no-next-rows", dest="next_rows", action="store_false",
                     help="skip the allocator and RoPE-store measurements")
     ap.add_argument("--no-graph", dest="graph", action="store_false", help="skip the decode graph measurements")
+    ap.add_argument("--separate-store", action="store_true",
+                    help="build_attn_metadata and kv_store as two calls (default: build_attn_metadata_store)")
     ap.add_argument("--layout", choices=["layer_first", "page_first", "row_interleaved"], default="layer_first",
                     help="physical order of a multi-layer KV cache whose layer 0 the step runs on")
     ap.add_argument("--layers", type=int, default=1, help="layers in that cache (1: a plain one-layer pool)")

@@ -185,6 +185,23 @@ int build_attn_metadata(const pkv_batch* batch, const pkv_page_table* page_table
                         int32_t num_qo_heads, int32_t num_kv_heads, const pkv_attn_metadata* meta,
                         void* stream);
 
+/* build_attn_metadata_store: build_attn_metadata followed by kv_store of the
+ * batch's new K/V rows at the out_loc rows it writes (the order the learning
+ * notes' store_kv passage gives: rows are placed before attention reads
+ * them), with identical results, in fewer launches: for a batch of at most
+ * 512 new tokens and 1024 requests (every decode step of the configurations
+ * here) one launch does both, its extra workgroups mapping 8 tokens each and
+ * copying their rows while the first builds the metadata; larger batches
+ * take the two calls' launches.  The pool's page_size and num_rows stand for
+ * build_attn_metadata's page_size and num_pool_rows, its num_kv_heads for
+ * num_kv_heads.
+ *   k_new, v_new : bf16 [num_tokens, Hkv, head_dim], contiguous, 16-byte aligned
+ * Tokens that get no row (out_loc -1) are not stored; padding tokens sharing
+ * the dummy row race as in kv_store.  Errors as the two calls'. */
+int build_attn_metadata_store(const pkv_batch* batch, const pkv_page_table* page_table, const pkv_kv_pool* pool,
+                              const int32_t* alloc_rows, int64_t num_alloc, int32_t num_qo_heads,
+                              const pkv_attn_metadata* meta, const void* k_new, const void* v_new, void* stream);
+
 /* paged_decode_attn: for each decode request i < num_decode and query head h,
  *   o[qo_indptr[i], h] = softmax(sm_scale * q[qo_indptr[i], h] . K[rows]^T) V[rows]
  * over rows = page_table[table_idx[i], 0 .. device_len[i]) (the new row stored
@@ -390,8 +407,8 @@ typedef struct pkv_decode_graph pkv_decode_graph;  /* opaque, host side */
 
 /* pkv_decode_graph_create: capture, for each batch size in sizes (host array,
  * strictly increasing, each <= max_reqs; the pages' list is 1, 2, 4, 8, 16, ...),
- * one graph of build_attn_metadata -> kv_store (at the metadata's out_loc) ->
- * paged_decode_attn on a decode batch of that many requests in desc's
+ * one graph of build_attn_metadata_store (metadata, then the rows at its
+ * out_loc) -> paged_decode_attn on a decode batch of that many requests in desc's
  * buffers.  stream must be a non-default stream (capture happens on it; the
  * buffers' contents are not read during capture).  This is the one call that
  * allocates: host memory and the graphs' driver objects, no device memory,

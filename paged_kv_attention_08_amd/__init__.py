@@ -23,6 +23,7 @@ from ._lib import (PKV_STATUS_BAD_ALLOC, PKV_STATUS_BAD_DECODE, PKV_STATUS_BAD_L
                    PKV_STATUS_FREE_OVERFLOW, PKV_STATUS_OUT_OF_PAGES, PKV_STATUS_TOKEN_COUNT)
 
 __all__ = ["PagedKVError", "KVPoolTensors", "KVCacheTensors", "BatchTensors", "MetadataBuffers", "kv_store", "build_attn_metadata",
+           "build_attn_metadata_store",
            "paged_decode_attn", "paged_decode_attn_static", "paged_extend_attn", "plan_bytes", "workspace_bytes", "library_path", "plan_view",
            "rope_cos_sin_cache", "kv_store_rope", "PKV_STATUS_BAD_POSITION", "DecodeGraph", "PageFreeList",
            "PKV_STATUS_OUT_OF_PAGES", "PKV_STATUS_FREE_OVERFLOW",
@@ -236,6 +237,28 @@ def build_attn_metadata(batch: BatchTensors, page_table: torch.Tensor, page_size
            _lib.lib().build_attn_metadata(ctypes.byref(b), ctypes.byref(pt), page_size, num_pool_rows,
                                           alloc_rows.data_ptr() if alloc_rows.numel() else None, alloc_rows.numel(),
                                           num_qo_heads, num_kv_heads, ctypes.byref(m), _stream(stream)))
+
+
+def build_attn_metadata_store(batch: BatchTensors, page_table: torch.Tensor, pool: KVPoolTensors,
+                              alloc_rows: torch.Tensor, num_qo_heads: int, meta: MetadataBuffers, k_new: torch.Tensor,
+                              v_new: torch.Tensor, stream=None) -> None:
+    """build_attn_metadata followed by kv_store of k_new / v_new at the
+    out_loc rows it writes, in one launch for small batches."""
+    b = batch.struct()
+    p = pool.struct()
+    _need(page_table, "page_table", torch.int32, 2)
+    _need(alloc_rows, "alloc_rows", torch.int32, 1)
+    _need(k_new, "k_new", torch.bfloat16, 3)
+    _need(v_new, "v_new", torch.bfloat16, 3)
+    if v_new.shape != k_new.shape or k_new.shape[1:] != pool.k.shape[1:] or k_new.shape[0] < batch.num_tokens:
+        raise ValueError("k_new / v_new shapes do not match the batch and pool")
+    pt = _lib.PageTable(page_table.data_ptr(), page_table.shape[0], page_table.shape[1])
+    m = meta.struct()
+    _check("build_attn_metadata_store",
+           _lib.lib().build_attn_metadata_store(ctypes.byref(b), ctypes.byref(pt), ctypes.byref(p),
+                                                alloc_rows.data_ptr() if alloc_rows.numel() else None,
+                                                alloc_rows.numel(), num_qo_heads, ctypes.byref(m), k_new.data_ptr(),
+                                                v_new.data_ptr(), _stream(stream)))
 
 
 def _attn(fn_name, pool, page_table, batch, meta, q, o, sm_scale, workspace, stream):

@@ -88,6 +88,8 @@ PROTOTYPES = {
     "pkv_plan_bytes": (c_size_t, [c_int32, c_int64, c_int32, c_int32]),
     "paged_attn_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
     "kv_store": (c_int, [POINTER(KVPool), c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p]),
+    "build_attn_metadata_store": (c_int, [POINTER(Batch), POINTER(PageTable), POINTER(KVPool), c_void_p, c_int64,
+                                          c_int32, POINTER(AttnMetadata), c_void_p, c_void_p, c_void_p]),
     "build_attn_metadata": (c_int, [POINTER(Batch), POINTER(PageTable), c_int32, c_int64, c_void_p, c_int64,
                                     c_int32, c_int32, POINTER(AttnMetadata), c_void_p]),
     "paged_decode_attn": (c_int, [POINTER(KVPool), POINTER(PageTable), POINTER(Batch), POINTER(AttnMetadata),

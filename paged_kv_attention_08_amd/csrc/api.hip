@@ -172,8 +172,49 @@ int prepare_metadata(const pkv_batch* batch, const pkv_page_table* page_table, i
   a.pad_from = INT32_MAX;
   a.dummy_row = 0;
   a.pad_table_idx = a.pad_cached_len = a.pad_device_len = a.pad_alloc_rows = nullptr;
+  a.k_new = a.v_new = nullptr;
+  a.k_pool = a.v_pool = nullptr;
+  a.store_stride_vec = 0;
+  a.store_row_vec = 0;
+  a.store_blocks = 0;
   *out = a;
   return PKV_OK;
+}
+
+int prepare_metadata_store(const pkv_batch* batch, const pkv_page_table* page_table, const pkv_kv_pool* pool,
+                           const int32_t* alloc_rows, int64_t num_alloc, int32_t num_qo_heads,
+                           const pkv_attn_metadata* meta, const void* k_new, const void* v_new, MetaArgs* a,
+                           StoreArgs* st) {
+  int rc = check_pool(pool);
+  if (rc != PKV_OK) return rc;
+  if ((rc = prepare_metadata(batch, page_table, pool->page_size, pool->num_rows, alloc_rows, num_alloc, num_qo_heads,
+                             pool->num_kv_heads, meta, a)) != PKV_OK)
+    return rc;
+  if (batch->num_tokens > 0 && (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)))
+    return PKV_ERR_INVALID_ARGUMENT;
+  a->k_new = static_cast<const uint4*>(k_new);
+  a->v_new = static_cast<const uint4*>(v_new);
+  a->k_pool = static_cast<uint4*>(pool->k);
+  a->v_pool = static_cast<uint4*>(pool->v);
+  a->store_stride_vec = pool->row_stride / 8;
+  a->store_row_vec = pool->num_kv_heads * pool->head_dim / 8;
+  st->k_new = a->k_new;
+  st->v_new = a->v_new;
+  st->out_loc = meta->out_loc;
+  st->k_pool = a->k_pool;
+  st->v_pool = a->v_pool;
+  st->num_tokens = batch->num_tokens;
+  st->row_stride_vec = a->store_stride_vec;
+  st->num_rows = pool->num_rows;
+  st->row_vec = a->store_row_vec;
+  st->status = meta->status;
+  return PKV_OK;
+}
+
+hipError_t launch_metadata_store(const MetaArgs& a, const StoreArgs& st, hipStream_t s) {
+  hipError_t e = launch_metadata(a, s);
+  if (e != hipSuccess || st.num_tokens == 0 || metadata_stores_rows(a)) return e;
+  return launch_kv_store(st, s);
 }
 
 }  // namespace pkv
@@ -221,6 +262,18 @@ int build_attn_metadata(const pkv_batch* batch, const pkv_page_table* page_table
                                   num_kv_heads, meta, &a);
   if (rc != PKV_OK) return rc;
   hipError_t e = launch_metadata(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : hip_failed(e);
+}
+
+int build_attn_metadata_store(const pkv_batch* batch, const pkv_page_table* page_table, const pkv_kv_pool* pool,
+                              const int32_t* alloc_rows, int64_t num_alloc, int32_t num_qo_heads,
+                              const pkv_attn_metadata* meta, const void* k_new, const void* v_new, void* stream) {
+  MetaArgs a;
+  StoreArgs st;
+  const int rc = prepare_metadata_store(batch, page_table, pool, alloc_rows, num_alloc, num_qo_heads, meta, k_new,
+                                        v_new, &a, &st);
+  if (rc != PKV_OK) return rc;
+  hipError_t e = launch_metadata_store(a, st, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : hip_failed(e);
 }
 

@@ -1,4 +1,4 @@
-// pkv_decode_graph_*: the decode step (build_attn_metadata -> kv_store ->
+// pkv_decode_graph_*: the decode step (build_attn_metadata_store ->
 // paged_decode_attn) captured once per padded batch size into HIP graphs and
 // replayed with one launch.
 //
@@ -34,7 +34,8 @@ using namespace pkv;
 namespace {
 
 // The step on a batch of bs decode requests, enqueued on s (captured by the
-// caller).  *plan_args receives the metadata plan kernel's argument block.
+// caller): build_attn_metadata_store, then paged_decode_attn.  *plan_args
+// receives the metadata plan kernel's argument block.
 int enqueue_step(const pkv_decode_graph_desc& d, int32_t bs, MetaArgs* plan_args, hipStream_t s) {
   pkv_batch b;
   b.num_reqs = bs;
@@ -44,8 +45,9 @@ int enqueue_step(const pkv_decode_graph_desc& d, int32_t bs, MetaArgs* plan_args
   b.cached_len = d.cached_len;
   b.device_len = d.device_len;
   MetaArgs a;
-  int rc = prepare_metadata(&b, &d.page_table, d.pool.page_size, d.pool.num_rows, d.alloc_rows, bs, d.num_qo_heads,
-                            d.pool.num_kv_heads, &d.meta, &a);
+  StoreArgs st;
+  int rc = prepare_metadata_store(&b, &d.page_table, &d.pool, d.alloc_rows, bs, d.num_qo_heads, &d.meta, d.k_new,
+                                  d.v_new, &a, &st);
   if (rc != PKV_OK) return rc;
   // padding: set per replay in the plan node's arguments (none at capture)
   a.pad_from = bs;
@@ -55,10 +57,9 @@ int enqueue_step(const pkv_decode_graph_desc& d, int32_t bs, MetaArgs* plan_args
   a.pad_device_len = d.device_len;
   a.pad_alloc_rows = d.alloc_rows;
   *plan_args = a;
-  hipError_t e = launch_metadata(a, s);
+  // metadata and store (one kernel for up to 512 requests), then attention
+  hipError_t e = launch_metadata_store(a, st, s);
   if (e != hipSuccess) return hip_failed(e);
-  rc = kv_store(&d.pool, d.k_new, d.v_new, d.meta.out_loc, bs, d.meta.status, s);
-  if (rc != PKV_OK) return rc;
   return paged_decode_attn(&d.pool, &d.page_table, &b, &d.meta, d.q, d.o, d.num_qo_heads, d.sm_scale, d.workspace,
                            d.workspace_bytes, s);
 }

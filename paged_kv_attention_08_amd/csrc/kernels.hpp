@@ -89,6 +89,16 @@ struct MetaArgs {
   int32_t* pad_cached_len;
   int32_t* pad_device_len;
   int32_t* pad_alloc_rows;
+  // Fused store (build_attn_metadata_store): when k_new is set and the batch
+  // is small enough for plan_kernel to map its tokens, workgroups 1..
+  // store_blocks of plan_kernel also copy the new K/V rows into the pool.
+  const uint4* k_new;
+  const uint4* v_new;
+  uint4* k_pool;
+  uint4* v_pool;
+  int64_t store_stride_vec;  // 16-byte vectors between pool rows
+  int32_t store_row_vec;     // 16-byte vectors per K (or V) row of a token
+  int32_t store_blocks;      // set by the launcher
 };
 
 struct AttnArgs {
@@ -125,6 +135,17 @@ hipError_t launch_free_pages(const AllocArgs& a, hipStream_t s);
 hipError_t launch_free_list_reset(int32_t* state, int32_t num_free, hipStream_t s);
 hipError_t launch_rope_cache(const RopeCacheArgs& a, hipStream_t s);
 hipError_t launch_metadata(const MetaArgs& a, hipStream_t s);
+// Whether launch_metadata(a) also stores the new K/V rows (a.k_new set and a
+// small batch); otherwise the caller launches kv_store after it.
+bool metadata_stores_rows(const MetaArgs& a);
+// build_attn_metadata_store's host checks and argument blocks, and its launches
+// (the store inside the metadata launch when metadata_stores_rows, else a
+// kv_store launch after it).
+int prepare_metadata_store(const pkv_batch* batch, const pkv_page_table* page_table, const pkv_kv_pool* pool,
+                           const int32_t* alloc_rows, int64_t num_alloc, int32_t num_qo_heads,
+                           const pkv_attn_metadata* meta, const void* k_new, const void* v_new, MetaArgs* a,
+                           StoreArgs* st);
+hipError_t launch_metadata_store(const MetaArgs& a, const StoreArgs& st, hipStream_t s);
 // Host checks of build_attn_metadata's arguments and its kernel argument block
 // (no padding).  Returns a PKV_* code.
 int prepare_metadata(const pkv_batch* batch, const pkv_page_table* page_table, int32_t page_size,

@@ -40,6 +40,7 @@ constexpr int kScanVals = 5;
 constexpr int kSortBuckets = 1024;  // extend tiles sorted by key count in steps of 64 keys (capped)
 constexpr int kFuseTokens = 512;    // new tokens plan_kernel maps itself
 constexpr int kFuseReqs = 1024;     // requests of such a batch (an LDS copy of qo_indptr)
+constexpr int kStoreTokens = 8;     // new tokens per store workgroup of a fused metadata + store launch
 static_assert(kSortBuckets % kPlanThreads == 0, "whole buckets per thread");
 
 struct ReqInfo {
@@ -105,21 +106,27 @@ __device__ inline void block_scan(int32_t (&v)[kScanVals], int32_t (&excl)[kScan
   __syncthreads();
 }
 
-// Token t of the batch (t < T): its request i (qo[i] <= t < qo[i + 1], by
-// binary search over qo, the running totals in global memory or LDS), its
-// logical position, and its row in the request's partial page or new pages;
-// writes page_table, out_loc and positions.  A token that gets no row is
-// marked -1 in out_loc and positions, so the store and RoPE calls skip it
-// instead of reusing a stale row.
-__device__ inline void map_token(const MetaArgs& a, int64_t t, const int32_t* qo, const int32_t* alloc_ptr) {
-  auto unmapped = [&]() {
-    a.out_loc[t] = -1;
-    a.positions[t] = -1;
-  };
-  if (t >= qo[a.B]) {  // fewer new tokens than num_tokens (flagged by plan_kernel)
-    unmapped();
-    return;
-  }
+// New tokens and new pages of request i (the running totals' terms; invalid
+// lengths count no pages, as the allocator gives them none).
+__device__ inline void req_counts(const MetaArgs& a, const ReqFields& f, int32_t* ext, int32_t* new_pages) {
+  const int32_t c = f.c, dl = f.dl, s = a.page_shift;
+  *ext = dl > c && c >= 0 ? dl - c : 0;
+  *new_pages = (c >= 0 && c <= dl) ? ceil_div_pow2(dl, s) - ceil_div_pow2(c, s) : 0;
+}
+
+// Token t of the batch: its request i (qo[i] <= t < qo[i + 1], by binary
+// search over qo, the running totals in global memory or LDS), its logical
+// position j, and its row in the request's partial page or new pages.  row is
+// -1 for a token that gets no row; bits holds the status bits a bad
+// page-table entry or alloc entry raises (an invalid request was already
+// reported by plan_kernel).
+struct TokenRow {
+  int32_t row, j, table_row, bits;
+};
+
+__device__ inline TokenRow token_row(const MetaArgs& a, int64_t t, const int32_t* qo, const int32_t* alloc_ptr) {
+  TokenRow out = {-1, -1, -1, 0};
+  if (t >= qo[a.B]) return out;  // fewer new tokens than num_tokens (flagged by plan_kernel)
   int lo = 0, hi = a.B;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -129,11 +136,7 @@ __device__ inline void map_token(const MetaArgs& a, int64_t t, const int32_t* qo
   const int i = lo;
   int32_t bits = 0;
   const ReqFields f = req_fields(a, i);
-  if (!request_ok(a, i, f, &bits)) {  // already reported by plan_kernel
-    unmapped();
-    return;
-  }
-  const int32_t r = f.r;
+  if (!request_ok(a, i, f, &bits)) return out;
   const int32_t c = f.c;
   const int32_t j = c + (int32_t)(t - qo[i]);
   const int32_t s = a.page_shift;
@@ -141,10 +144,9 @@ __device__ inline void map_token(const MetaArgs& a, int64_t t, const int32_t* qo
   const int32_t first_new_page = ceil_div_pow2(c, s);
   const int32_t lp = j >> s;
   int64_t row;
-  int32_t* pt_row = a.page_table + (int64_t)r * a.W;
   if (lp < first_new_page) {
-    // the request's partially filled last cached page
-    row = (int64_t)pt_row[j - slot] + slot;
+    // the request's partially filled last cached page (an entry before cached_len)
+    row = (int64_t)a.page_table[(int64_t)f.r * a.W + (j - slot)] + slot;
     if (row < 0 || row >= a.num_pool_rows) bits |= PKV_STATUS_BAD_PAGE_ROW;
   } else if (i >= a.pad_from) {
     row = slot;  // a padding request's one new row: the dummy page
@@ -159,14 +161,80 @@ __device__ inline void map_token(const MetaArgs& a, int64_t t, const int32_t* qo
       if (pr < 0 || (pr & ((1 << s) - 1)) != 0 || row >= a.num_pool_rows) bits |= PKV_STATUS_BAD_ALLOC;
     }
   }
-  if (bits) {
-    raise_status(a.status, bits);
-    unmapped();
+  out.bits = bits;
+  if (!bits) {
+    out.row = (int32_t)row;
+    out.j = j;
+    out.table_row = f.r;
+  }
+  return out;
+}
+
+// Writes page_table, out_loc and positions of token t.  A token that gets no
+// row is marked -1 in out_loc and positions, so the store and RoPE calls skip
+// it instead of reusing a stale row.
+__device__ inline void map_token(const MetaArgs& a, int64_t t, const int32_t* qo, const int32_t* alloc_ptr) {
+  const TokenRow tr = token_row(a, t, qo, alloc_ptr);
+  if (tr.bits) raise_status(a.status, tr.bits);
+  if (tr.row < 0) {
+    a.out_loc[t] = -1;
+    a.positions[t] = -1;
     return;
   }
-  pt_row[j] = (int32_t)row;
-  a.out_loc[t] = (int32_t)row;
-  a.positions[t] = j;
+  a.page_table[(int64_t)tr.table_row * a.W + tr.j] = tr.row;
+  a.out_loc[t] = tr.row;
+  a.positions[t] = tr.j;
+}
+
+// A store workgroup of the fused metadata + store launch (workgroups 1.. of
+// plan_kernel): it rebuilds the two running totals it needs (new tokens and
+// new pages per request) in LDS, maps its kStoreTokens tokens to rows as
+// map_token does and copies their K and V rows into the pool, consecutive
+// threads on consecutive 16-byte vectors of a row.  Workgroup 0 writes the
+// metadata meanwhile; the mapping here reads only page-table entries before
+// each request's cached_len, which workgroup 0 does not write.
+__device__ inline void store_block(const MetaArgs& a, int32_t* s_qo, int32_t* s_ap, int32_t (*smem)[kPlanWaves],
+                                   int32_t* s_rows) {
+  const int tid = threadIdx.x;
+  int32_t carry_q = 0, carry_a = 0;
+  if (tid == 0) {
+    s_qo[0] = 0;
+    s_ap[0] = 0;
+  }
+  for (int base = 0; base < a.B; base += kPlanThreads) {
+    const int i = base + tid;
+    int32_t ext = 0, np = 0;
+    if (i < a.B) req_counts(a, req_fields(a, i), &ext, &np);
+    int32_t v[kScanVals] = {ext, np, 0, 0, 0};
+    int32_t ex[kScanVals], tot[kScanVals];
+    block_scan(v, ex, tot, smem);
+    if (i < a.B) {
+      s_qo[i + 1] = carry_q + ex[0] + ext;
+      s_ap[i + 1] = carry_a + ex[1] + np;
+    }
+    carry_q += tot[0];
+    carry_a += tot[1];
+  }
+  __syncthreads();
+  const int64_t t0 = (int64_t)(blockIdx.x - 1) * kStoreTokens;
+  if (tid < kStoreTokens) {
+    const int64_t t = t0 + tid;
+    s_rows[tid] = t < a.T ? token_row(a, t, s_qo, s_ap).row : -1;
+  }
+  __syncthreads();
+  const int rv = a.store_row_vec;
+  for (int idx = tid; idx < kStoreTokens * rv; idx += kPlanThreads) {
+    const int k = idx / rv;
+    const int c = idx - k * rv;
+    const int32_t row = s_rows[k];
+    if (row < 0) continue;  // past the batch's tokens, or a token that got no row
+    const int64_t src = (t0 + k) * rv + c;
+    const uint4 kv = a.k_new[src];
+    const uint4 vv = a.v_new[src];
+    const int64_t dst = (int64_t)row * a.store_stride_vec + c;
+    a.k_pool[dst] = kv;
+    a.v_pool[dst] = vv;
+  }
 }
 
 __global__ void __launch_bounds__(256) token_kernel(MetaArgs a) {
@@ -178,6 +246,12 @@ __global__ void __launch_bounds__(256) token_kernel(MetaArgs a) {
 __global__ void __launch_bounds__(kPlanThreads) plan_kernel(MetaArgs a) {
   __shared__ int32_t smem[kScanVals][kPlanWaves];
   __shared__ int32_t s_qo[kFuseReqs + 1];  // qo_indptr of a fused batch
+  if (blockIdx.x > 0) {  // a store workgroup (uniform for the workgroup)
+    __shared__ int32_t s_ap[kFuseReqs + 1];
+    __shared__ int32_t s_rows[kStoreTokens];
+    store_block(a, s_qo, s_ap, smem, s_rows);
+    return;
+  }
   const int tid = threadIdx.x;
   int32_t bits = 0;
   int32_t* header = (int32_t*)a.plan;
@@ -207,12 +281,10 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(MetaArgs a) {
         a.pad_cached_len[i] = f.c;
         a.pad_device_len[i] = f.dl;
       }
-      const int32_t c = f.c;
       const int32_t dl = f.dl;
       ri.valid = request_ok(a, i, f, &bits);
-      ri.ext = dl > c && c >= 0 ? dl - c : 0;
+      req_counts(a, f, &ri.ext, &ri.new_pages);
       ri.dl = dl > 0 ? dl : 0;
-      ri.new_pages = (c >= 0 && c <= dl) ? ceil_div_pow2(dl, s) - ceil_div_pow2(c, s) : 0;
       if (ri.valid) {
         if (i < a.num_decode) ri.dtiles = (dl + kDecodeTileKeys - 1) / kDecodeTileKeys;
         else ri.tiles = (ri.ext + tq - 1) / tq;
@@ -315,6 +387,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(MetaArgs a) {
 MetaArgs metadata_launch_args(const MetaArgs& a_in) {
   MetaArgs a = a_in;
   a.fuse_tokens = (a.T <= kFuseTokens && a.B <= kFuseReqs) ? 1 : 0;
+  a.store_blocks = (a.k_new && a.fuse_tokens && a.T > 0) ? (int32_t)((a.T + kStoreTokens - 1) / kStoreTokens) : 0;
   return a;
 }
 
@@ -322,7 +395,7 @@ MetaArgs metadata_launch_args(const MetaArgs& a_in) {
 
 hipError_t launch_metadata(const MetaArgs& a_in, hipStream_t s) {
   const MetaArgs a = metadata_launch_args(a_in);
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
+  hipLaunchKernelGGL(plan_kernel, dim3(1 + a.store_blocks), dim3(kPlanThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.T == 0 || a.fuse_tokens) return e;
   const int64_t blocks = (a.T + 255) / 256;
@@ -330,11 +403,13 @@ hipError_t launch_metadata(const MetaArgs& a_in, hipStream_t s) {
   return hipGetLastError();
 }
 
+bool metadata_stores_rows(const MetaArgs& a) { return metadata_launch_args(a).store_blocks > 0; }
+
 void metadata_plan_node(const MetaArgs& a, MetaArgs* args, void** argv, hipKernelNodeParams* p) {
   *args = metadata_launch_args(a);
   argv[0] = args;
   p->func = reinterpret_cast<void*>(plan_kernel);
-  p->gridDim = dim3(1);
+  p->gridDim = dim3(1 + args->store_blocks);
   p->blockDim = dim3(kPlanThreads);
   p->sharedMemBytes = 0;
   p->kernelParams = argv;

@@ -11,8 +11,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (BatchTensors, KVPoolTensors, MetadataBuffers, build_attn_metadata, kv_store, paged_decode_attn,
-               paged_extend_attn, plan_view, workspace_bytes)
+from . import (BatchTensors, KVPoolTensors, MetadataBuffers, build_attn_metadata, build_attn_metadata_store,
+               kv_store, paged_decode_attn, paged_extend_attn, plan_view, workspace_bytes)
 
 BF16_NAN_BITS = 0x7FC0
 
@@ -74,6 +74,12 @@ class DeviceStep:
     def store(self, stream=None):
         kv_store(self.pool, self.k_new, self.v_new, self.meta.out_loc[:self.w.num_tokens], self.meta.status, stream)
 
+    def metadata_store(self, stream=None):
+        """metadata and store in one call (build_attn_metadata_store)."""
+        w = self.w
+        build_attn_metadata_store(self.batch, self.page_table, self.pool, self.alloc_rows, w.num_qo_heads, self.meta,
+                                  self.k_new, self.v_new, stream)
+
     def decode(self, stream=None):
         paged_decode_attn(self.pool, self.page_table, self.batch, self.meta, self.q, self.o, self.w.sm_scale,
                           self.workspace, stream)
@@ -82,9 +88,12 @@ class DeviceStep:
         paged_extend_attn(self.pool, self.page_table, self.batch, self.meta, self.q, self.o, self.w.sm_scale,
                           None, stream)
 
-    def run(self, stream=None):
-        self.metadata(stream)
-        self.store(stream)
+    def run(self, stream=None, fused_store: bool = False):
+        if fused_store:
+            self.metadata_store(stream)
+        else:
+            self.metadata(stream)
+            self.store(stream)
         self.decode(stream)
         self.extend(stream)
 

@@ -217,6 +217,25 @@ def test_static_scratch_size_is_the_stated_one(lib):
     assert lib.paged_attn_workspace_bytes(1, 16, 128) > _lib.PKV_STATIC_SCRATCH_BYTES
 
 
+def test_metadata_store_rejects(lib):
+    """build_attn_metadata_store checks like its two calls, before any launch."""
+    f = lib.build_attn_metadata_store
+    ok = dict(b=batch(), t=table(), p=pool(), alloc=FAKE, n=4, hq=32, m=meta(), k=FAKE, v=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(B(a["b"]), B(a["t"]), B(a["p"]), a["alloc"], a["n"], a["hq"], B(a["m"]), a["k"], a["v"], None)
+
+    assert call(p=pool(head_dim=64)) == _lib.PKV_ERR_UNSUPPORTED
+    assert call(p=pool(k=None)) == _lib.PKV_ERR_INVALID_ARGUMENT
+    assert call(k=None) == _lib.PKV_ERR_INVALID_ARGUMENT
+    assert call(v=FAKE + 4) == _lib.PKV_ERR_INVALID_ARGUMENT
+    assert call(hq=12) == _lib.PKV_ERR_INVALID_ARGUMENT
+    assert call(alloc=None) == _lib.PKV_ERR_INVALID_ARGUMENT
+    assert call(m=meta(plan_bytes=8)) == _lib.PKV_ERR_WORKSPACE
+    assert call(t=table(width=31)) == _lib.PKV_ERR_INVALID_ARGUMENT
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(_lib, "_LIB", None)

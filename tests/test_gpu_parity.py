@@ -27,12 +27,12 @@ pytestmark = pytest.mark.gpu
 WHOLE_POOL_MAX_ROWS = 1 << 22  # a copy of pools up to 16 GiB (K + V) is taken for the diff
 
 
-def run_case(w, decode_requests=None, extend_tokens=None, label=""):
+def run_case(w, decode_requests=None, extend_tokens=None, label="", fused_store=False):
     log(f"case {label}: {w.summary()}")
     ds = DeviceStep(w)
     before = ds.snapshot_pool() if w.num_pool_rows <= WHOLE_POOL_MAX_ROWS else None
-    log("  device step")
-    ds.run()
+    log("  device step" + (" (metadata and store in one call)" if fused_store else ""))
+    ds.run(fused_store=fused_store)
     torch.cuda.synchronize()
     log("  device step done")
     assert ds.status() == 0, f"device status bits {ds.status():#x}"
@@ -325,4 +325,24 @@ def test_empty_batch():
     torch.cuda.synchronize()
     assert ds.status() == 0
     assert int(ds.meta.qo_indptr[0].item()) == 0 and int(ds.meta.kv_indptr[0].item()) == 0
+    ds.free()
+
+
+FUSED_CASES = ["small1", "small2", "small3", "small4", "small5", "full1", "full2", "single_key", "group16", "kv3",
+               "page2", "page16", "page32", "seq_pages64", "meta512", "meta513"]
+
+
+@pytest.mark.parametrize("name", FUSED_CASES)
+def test_metadata_and_store_in_one_call(name):
+    """build_attn_metadata_store gives what build_attn_metadata + kv_store give:
+    the same bit-exact metadata, stored rows and untouched pool, and outputs
+    within the bar (one launch up to 512 new tokens: meta512; two above:
+    meta513)."""
+    if name.startswith("small"):
+        w = configs.small(int(name[5:]))
+    elif name.startswith("full"):
+        w = configs.FULL[int(name[4:])]()
+    else:
+        w = dict(_edge_workloads())[name]
+    ds, _, _ = run_case(w, label=f"fused {name}", fused_store=True)
     ds.free()
