@@ -381,6 +381,23 @@ def measure(cfg, args, torch, flush_buf):
         out["decode_unflushed_ms"] = round(unflushed_ms, 4)
     if "kv_store" in parts:
         out["store_gbps"] = round(st_bytes / (float(parts["kv_store"]) * 1e-3) / 1e9, 1)
+    elif w.num_tokens > 512:
+        # the store of a large batch on its own (the step runs it inside
+        # build_attn_metadata_store); repeating it writes the same rows
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            if flushed:
+                flush()
+            e0.record(stream)
+            ds.store()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        st_ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
+        out["kv_store_ms"] = round(st_ms, 4)
+        out["store_gbps"] = round(st_bytes / (st_ms * 1e-3) / 1e9, 1)
+    if "store_gbps" in out:
+        out["store_frac_hbm"] = round(out["store_gbps"] / PM.HBM_PEAK_GBPS, 4)
     if decode_dominant:
         roof = {"bound": "hbm", "achieved": out["decode_gbps"], "peak": PM.HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": out["decode_frac_hbm"], "traffic": traffic, "kernel": "decode_kernel + decode_merge_kernel",
