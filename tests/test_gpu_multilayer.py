@@ -31,18 +31,24 @@ def layer_workload(w, layer):
 @pytest.mark.parametrize("layout", [pkv.KVCacheTensors.LAYER_FIRST, pkv.KVCacheTensors.PAGE_FIRST,
                                     pkv.KVCacheTensors.ROW_INTERLEAVED],
                          ids=["layer_first", "page_first", "row_interleaved"])
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "one_call"])
 @pytest.mark.parametrize("cfg", [2, 5])
-def test_each_layer_matches_oracle(layout, cfg):
+def test_each_layer_matches_oracle(layout, cfg, fused):
+    """fused: metadata and store through build_attn_metadata_store, whose store
+    workgroups take the layer's row stride."""
     w = configs.small(cfg)
-    log(f"multi-layer cache layout {layout} config {cfg}: {w.summary()}")
+    log(f"multi-layer cache layout {layout} config {cfg} fused {fused}: {w.summary()}")
     cache = pkv.KVCacheTensors(L, w.num_pool_rows, w.num_kv_heads, w.head_dim, w.page_size, layout)
     steps = [DeviceStep(layer_workload(w, l), pool=cache.layer(l)) for l in range(L)]
     torch.cuda.synchronize()
     snap = lambda s: (s.k_pool.clone(), s.v_pool.clone())
     before = [snap(s) for s in steps]
     for l, ds in enumerate(steps):
-        ds.metadata()
-        ds.store()
+        if fused:
+            ds.metadata_store()
+        else:
+            ds.metadata()
+            ds.store()
         if w.num_decode:
             ds.decode()
         if w.num_decode < w.num_reqs:

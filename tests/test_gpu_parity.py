@@ -12,6 +12,8 @@ positions (first row, last row, tile, page and decode-run boundaries), where a
 dropped or shifted key would otherwise hide in the small N(0,1) outputs of
 long contexts.
 """
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -239,7 +241,9 @@ def test_attention_repeated_on_one_plan(which):
     ds.free()
 
 
+@functools.lru_cache(maxsize=1)
 def _edge_workloads():
+    """The edge-case batches (built once per session; the tests do not modify them)."""
     cases = []
     # every request has a single key: the output is that key's V, exactly
     cases.append(("single_key", build_workload("single_key", 41, [RequestSpec(0, 1) for _ in range(5)],
@@ -295,6 +299,17 @@ def _edge_workloads():
         cases.append((f"meta{nreq}", build_workload(f"meta{nreq}", 62 + nreq % 2, reqs, num_qo_heads=32,
                                                     num_kv_heads=8, head_dim=128, page_size=1,
                                                     num_pool_rows=1 << 18, num_decode=nreq)))
+    # the largest query-head group (16 per KV head: the largest decode workspace) at long-decode lengths
+    cases.append(("group16_long", build_workload("group16_long", 64, [RequestSpec(17000, 17001),
+                                                                      RequestSpec(30001, 30002),
+                                                                      RequestSpec(20000, 20004)],
+                                                 num_qo_heads=128, num_kv_heads=8, head_dim=128, page_size=1,
+                                                 num_pool_rows=1 << 17, num_decode=2)))
+    # 4096 decode requests: past the plan kernel's LDS copy of the running totals (1024 requests)
+    lens = [(53 * k) % 97 + 1 for k in range(4096)]
+    cases.append(("batch4096", build_workload("batch4096", 65, [RequestSpec(l, l + 1) for l in lens],
+                                              num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=1,
+                                              num_pool_rows=1 << 19, num_decode=4096)))
     # one long decode request spread over many splits, width exactly its length rounded to 32
     cases.append(("long_single", build_workload("long_single", 50, [RequestSpec(20000, 20001)],
                                                 num_qo_heads=64, num_kv_heads=8, head_dim=128, page_size=1,
@@ -329,7 +344,7 @@ def test_empty_batch():
 
 
 FUSED_CASES = ["small1", "small2", "small3", "small4", "small5", "full1", "full2", "single_key", "group16", "kv3",
-               "page2", "page16", "page32", "seq_pages64", "meta512", "meta513"]
+               "page2", "page16", "page32", "seq_pages64", "meta512", "meta513", "batch4096"]
 
 
 @pytest.mark.parametrize("name", FUSED_CASES)
