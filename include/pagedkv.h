@@ -12,9 +12,16 @@
  *   kv_store             scatter of the new K/V rows to their out_loc rows
  *   paged_decode_attn    split-K decode attention (one new token per request)
  *   paged_extend_attn    chunked-prefill attention on a cached prefix
+ * and around them:
+ *   build_attn_metadata_store  the first two in one launch for small batches
+ *   paged_decode_attn_static   decode attention that allocates nothing
  *   kv_store_rope        kv_store with rotary position embedding (and an
  *                        optional per-head RMS norm) applied to q and k on
  *                        the way (deep dive sections 7.2-7.3)
+ *   pkv_alloc_pages / pkv_free_pages   the page free list on the device
+ *   pkv_decode_graph_*   the decode step captured as HIP graphs
+ *   pkv_kv_cache_layer   one layer of a multi-layer KV cache
+ *   pkv_plan_view_layout where the plan keeps its work lists
  *
  * Conventions shared by every entry point
  *   - Every pointer inside the structs and every data argument is a DEVICE
