@@ -163,3 +163,28 @@ def test_kv_store_rope_full_size_sampled(cfg):
     locs = inp.out_loc[idx].astype(np.int64)
     assert_rows_close(bits(k_pool[torch.from_numpy(locs).cuda()]), np.stack([rows[int(r)][0] for r in locs]), "k")
     assert np.array_equal(bits(v_pool[torch.from_numpy(locs).cuda()]), np.stack([rows[int(r)][1] for r in locs]))
+
+
+def test_kv_store_rope_whole_token_grid_with_bad_entries():
+    """At 512 tokens or more a workgroup takes a whole token (below, a 16-row
+    chunk): 700 tokens of 36 rows (the last 16-row pass partial), qk-norm,
+    one position past the table and one row outside the pool."""
+    T, hq, hkv = 700, 32, 2
+    inp = rope_inputs(37, T, hq, hkv, max_position=8192)
+    inp.positions[5] = 8192
+    inp.out_loc[9] = inp.num_pool_rows
+    q, k_pool, v_pool, st = run_rope(inp, hq, hkv, 1e6, True)
+    assert st == (pkv.PKV_STATUS_BAD_POSITION | pkv.PKV_STATUS_BAD_OUT_LOC)
+    qb = bits(q)
+    assert np.array_equal(qb[5], inp.q[5])
+    assert not bits(v_pool[int(inp.out_loc[5])]).any()
+    ok = np.setdiff1d(np.arange(T), [5, 9])
+    q_ref, rows = R.store_kv_rope(inp.q[ok], inp.k[ok], inp.v[ok], inp.out_loc[ok], inp.positions[ok], 1e6,
+                                  (inp.q_weight, inp.k_weight, NORM_EPS))
+    assert_rows_close(qb[ok], q_ref, "q")
+    q9, _ = R.store_kv_rope(inp.q[[9]], inp.k[[9]], inp.v[[9]], np.array([0]), inp.positions[[9]], 1e6,
+                            (inp.q_weight, inp.k_weight, NORM_EPS))
+    assert_rows_close(qb[[9]], q9, "q of the token with a bad row")
+    locs = inp.out_loc[ok].astype(np.int64)
+    assert_rows_close(bits(k_pool[torch.from_numpy(locs).cuda()]), np.stack([rows[int(r)][0] for r in locs]), "k")
+    assert np.array_equal(bits(v_pool[torch.from_numpy(locs).cuda()]), np.stack([rows[int(r)][1] for r in locs]))
