@@ -19,15 +19,20 @@
 // the same L2.
 //
 // Per 64-key tile:
-//   * the workgroup gathers 64 K rows and 64 V rows of head g into registers
-//     two tiles ahead (two register sets, page-table entries one tile before
-//     that): wavefront w takes keys 8w..8w+7, each 16-lane group one whole
-//     256-byte head row per load (16 bytes per lane), so a load instruction
-//     touches 4 rows.  (With one key per lane, every instruction touched 64
-//     scattered rows and half the address translations missed the per-CU
-//     TLB.)  Both tiles are stored row-major ([key][d]) in LDS as contiguous
-//     256-byte runs, in two stages: tile n + 1 is stored while tile n is in
-//     use, so one barrier per tile suffices;
+//   * the workgroup gathers 64 K rows and 64 V rows of head g straight into
+//     LDS (global_load_lds_dwordx4: the data never passes through registers)
+//     three tiles ahead, into four LDS stages (tile n in stage n % 4):
+//     wavefront w takes keys 8w..8w+7, each 16-lane group one whole 256-byte
+//     head row per load (16 bytes per lane), so a load instruction fills 4
+//     rows, 1 KB contiguous in LDS.  (With one key per lane, every
+//     instruction touched 64 scattered rows and half the address
+//     translations missed the per-CU TLB.)  Rows are unpadded; their 16-byte
+//     chunks are permuted (a XOR swizzle chosen when the row is gathered) so
+//     that the operand reads below hit distinct LDS banks.  The page-table
+//     entries travel the same way, into a small per-wavefront ring, six tiles
+//     ahead.  These loads and every wait for them are written out by hand
+//     (the compiler would wait for all of them before any LDS read); one
+//     barrier per tile;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys x rows): the K operand
 //     is read from LDS, Q stays in registers for the whole loop.  In the
 //     32x32 accumulator layout each lane owns one row (query) and 16 of its 32
@@ -54,12 +59,39 @@ namespace {
 
 constexpr int kKeyTile = 64;
 constexpr int kVW = 4;  // V^T operand reads in flight ahead of the PV MFMAs
-constexpr int kKsStride = 136;  // bf16 elements per K row in LDS (128 + 8 pad)
-constexpr int kVsStride = 160;  // bf16 elements per V row in LDS (80 dwords: 4 rows x 16 dwords hit 64 distinct banks)
 constexpr int kWaves = 8;
 static_assert(kExtendRows == 32 * kWaves, "one 32-row block per wavefront");
 constexpr int kWaveKeys = kKeyTile / kWaves;  // keys of a tile one wavefront gathers
 constexpr int kLoads = kWaveKeys / 4;         // 16-byte loads per lane per tile and per K / V (4 rows per load)
+static_assert(kLoads == 2, "two 4-row loads per wavefront and operand");
+constexpr int kStages = 4;                                       // LDS stages: tile n in stage n % 4
+constexpr int kTileBytes = kKeyTile * kHeadDim * 2;              // 16 KB, unpadded rows
+constexpr int kVRegion = kStages * kTileBytes;                   // V tiles after the K tiles
+constexpr int kRingOff = 2 * kVRegion;                           // page-table entry ring
+constexpr int kRingSlots = 4;
+constexpr int kRingWave = 256;                                   // bytes per wavefront and slot
+constexpr int kLdsBytes = kRingOff + kRingSlots * kWaves * kRingWave;
+static_assert(kLdsBytes <= 160 * 1024, "fits the CU's LDS");
+// Every K operand read (stage, 32-key block) and V operand read (stage,
+// block, 16-key half) is a 16-bit immediate offset from a per-lane base: the
+// K stages fill the first 64 KB and the V stages the next.
+static_assert((kStages - 1) * kTileBytes + 8192 < 65536, "K read offsets fit the immediate field");
+// Load schedule, per iteration n (tile n): the entries of tile n + kEntryLead,
+// the rows of tile n + kRowLead (from entries read into registers during
+// iteration n - 1).  Exactly kOpsPerTile vector-memory instructions per
+// iteration and wavefront.
+constexpr int kRowOps = 2 * kLoads;                 // K and V row loads per iteration
+constexpr int kOpsPerTile = 1 + kRowOps;            // + one entry load
+constexpr int kRowLead = kStages - 1;               // rows of tile n + 3
+constexpr int kEntryLead = kRowLead + 3;            // entries of tile n + 6
+static_assert(kEntryLead - kRowLead < kRingSlots, "ring slots outlive their reads");
+// Rows of tile n + 1 (issued in iteration n - 2) are followed by two whole
+// iterations' ops when iteration n ends.
+constexpr int kWaitRows = 2 * kOpsPerTile;
+// Entries of tile n + 4 (issued first in iteration n - 2) are followed by the
+// row loads of iteration n - 2 and two whole iterations when iteration n has
+// issued its rows.
+constexpr int kWaitEntries = kRowOps + 2 * kOpsPerTile;
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 
@@ -70,10 +102,28 @@ __device__ inline float dot2_bf16(uint32_t w, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w), __builtin_bit_cast(bf16x2v, 0x3F803F80u), acc, false);
 }
 
+// Swizzle of a tile row's 16 16-byte chunks: logical chunk c of row r sits in
+// slot c ^ swz(r).  Any 16 consecutive rows map one logical chunk to 16
+// distinct slots (the K operand reads: 16 lanes, 16 rows, one chunk), and any
+// 4 rows 4-aligned put chunks 4b..4b+3 in 16 distinct slots (the transpose
+// reads of V: 4 rows x 4 chunks per 32 lanes), so neither read conflicts.
+__device__ inline int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// Loads that write LDS directly (the data never passes through registers).
+// They are issued as inline assembly so that the compiler, which would
+// otherwise wait for every such load before any LDS read, leaves them in
+// flight; every wait for them below is explicit.  Lane l's bytes land at LDS
+// byte address m0 + size * l.  One wait state is needed between the write of
+// m0 and its read by the load.
+__device__ inline void lds_load16(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(g) : "memory", "m0");
+}
+__device__ inline void lds_load4(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_addr), "v"(g) : "memory", "m0");
+}
+
 __global__ void __launch_bounds__(64 * kWaves, 8 / kWaves) extend_kernel(AttnArgs a) {
-  // two LDS stages: tile n lives in stage n % 2
-  __shared__ __attribute__((aligned(16))) uint16_t ks_all[2][kKeyTile * kKsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t vs_all[2][kKeyTile * kVsStride];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
 
   const int32_t* header = reinterpret_cast<const int32_t*>(a.plan);
   // Workgroups are dispatched to the 8 XCDs round-robin (linear id % 8) and
@@ -101,7 +151,7 @@ __global__ void __launch_bounds__(64 * kWaves, 8 / kWaves) extend_kernel(AttnArg
   const int TQ = a.layout.tile_q;
   const int n_tok = min(TQ, dl - c - t0);
 
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5;
   const int l32 = lane & 31;
@@ -123,50 +173,110 @@ __global__ void __launch_bounds__(64 * kWaves, 8 / kWaves) extend_kernel(AttnArg
   }
 
   const int kv_end = min(dl, c + t0 + n_tok);
+  const int n_kt = (kv_end + kKeyTile - 1) / kKeyTile;  // key tiles of the item
   const int32_t* pt_row = a.page_table + (int64_t)a.table_idx[i] * a.W;
-  const uint16_t* kbase = a.k_pool + (int64_t)g * kHeadDim + (lane & 15) * 8;
-  const uint16_t* vbase = a.v_pool + (int64_t)g * kHeadDim + (lane & 15) * 8;
   const uint32_t row_elems = (uint32_t)a.row_stride;  // < 2^31, checked on the host
   const uint32_t n_rows = (uint32_t)a.num_pool_rows;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
 
-  // loader: load u (0..kLoads-1) of lane l in wavefront w moves 16 bytes
-  // (dims 8 (l % 16) ..) of key kWaveKeys w + 4 u + l / 16 of the tile.  Keys past kv_end
-  // re-read the last valid key's row: finite data, and such keys only occur in the
-  // last tile, which is always masked, so their probabilities are exactly 0.  Tiles
-  // past the end are gathered the same way: every tile issues the same loads, which
-  // lets the compiler wait only for the loads of the tile being stored (with
-  // conditional gathers it waited for the previous tile's loads as well, halving
-  // the prefetch distance).
-  uint4 kpre[2][kLoads], vpre[2][kLoads];  // [register set][load]
-  // page-table entries of the next tile to gather, one per load (16 lanes share one)
-  int32_t ent[kLoads];
-  auto load_entries = [&](int kt) __attribute__((always_inline)) {
+  // Gather of tile n (keys 64 n ..): load u (0, 1) of lane l in wavefront w
+  // moves the 16-byte chunk that belongs in slot l % 16 of tile row
+  // 8 w + 4 u + l / 16, i.e. logical chunk (l % 16) ^ swz(row), so one
+  // instruction fills 4 whole rows (1 KB, contiguous in LDS).  Keys past
+  // kv_end re-read the last valid key's row: finite data, only in the last
+  // tile, which is always masked, so their probabilities are exactly 0; tiles
+  // past the end are gathered the same way, so every tile issues the same
+  // loads and the explicit wait counts hold on every path.
+  const uint16_t* kbase = a.k_pool + (int64_t)g * kHeadDim;
+  const uint16_t* vbase = a.v_pool + (int64_t)g * kHeadDim;
+  uint32_t chunk_el[kLoads];
 #pragma unroll
-    for (int u = 0; u < kLoads; ++u) ent[u] = pt_row[min(kt + kWaveKeys * wave + 4 * u + (lane >> 4), kv_end - 1)];
+  for (int u = 0; u < kLoads; ++u) chunk_el[u] = (uint32_t)(((lane & 15) ^ swz(4 * u + (lane >> 4))) * 8);
+  // (8 w + 4 u + l / 16) & 15 = 4 u + l / 16 + 8 (w & 1); swz depends on the
+  // row's low 4 bits, and 8 (w & 1) only sets bit 3
+  if (wave & 1) {
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) chunk_el[u] = (uint32_t)(((lane & 15) ^ swz(8 + 4 * u + (lane >> 4))) * 8);
+  }
+
+  // Page-table entries of tile n (keys 8 w .. 8 w + 7 of each wavefront) go
+  // to ring slot n % 4 of the wavefront: lane l loads key 8 w + l % 8 (the
+  // eight copies are harmless), lane l later reads keys 8 w + 4 u + l / 16.
+  // A slot is written in iteration n - 6 and read in iteration n - 4; the
+  // next write to it comes in iteration n - 2.
+  const uint32_t ring = lds_base + kRingOff + wave * kRingWave;
+  auto load_entries = [&](int n) __attribute__((always_inline)) {
+    const int key = min(n * kKeyTile + kWaveKeys * wave + (lane & 7), kv_end - 1);
+    lds_load4(pt_row + key, ring + (uint32_t)((n & (kRingSlots - 1)) * kWaves * kRingWave));
   };
-  auto gather = [&](int kt, auto set_tag) __attribute__((always_inline)) {
-    constexpr int SET = decltype(set_tag)::value;
+  // Issue step of iteration n: the entries of tile n + 6, then the K/V rows of
+  // tile n + 3 (into the stage of tile n - 1, which every wavefront finished
+  // before the last barrier) from the entries read into registers during the
+  // previous iteration, then, for the next iteration, the entries of tile
+  // n + 4 from the ring.  A status atomic on a bad row only adds
+  // vector-memory ops, which makes every count-based wait stricter.
+  uint32_t ent[kLoads];
+  auto read_entries = [&](int m) __attribute__((always_inline)) {
+    const uint32_t slot = (uint32_t)kRingOff + wave * kRingWave + (uint32_t)((m & (kRingSlots - 1)) * kWaves * kRingWave);
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) ent[u] = *reinterpret_cast<const uint32_t*>(lds + slot + 4 * (4 * u + (lane >> 4)));
+  };
+  auto issue = [&](int n) __attribute__((always_inline)) {
+    load_entries(n + kEntryLead);
+    const int m = n + kRowLead;
     uint32_t r[kLoads];
     bool bad = false;
 #pragma unroll
     for (int u = 0; u < kLoads; ++u) {
-      r[u] = (uint32_t)ent[u];
+      r[u] = ent[u];
       const bool b = r[u] >= n_rows;  // also catches negative entries
       bad |= b;
       r[u] = b ? 0u : r[u];
     }
-    // the next tile's entries are requested before this tile's rows, so the
-    // wait for them (one tile later) can leave these row loads in flight
-    load_entries(kt + kKeyTile);
-    // 32 x 32 -> 64-bit row offsets
+    const uint32_t stage_k = lds_base + (uint32_t)((m & (kStages - 1)) * kTileBytes);
 #pragma unroll
     for (int u = 0; u < kLoads; ++u) {
-      const uint64_t off = (uint64_t)r[u] * row_elems;
-      kpre[SET][u] = load16(kbase + off);
-      vpre[SET][u] = load16(vbase + off);
+      const uint64_t off = (uint64_t)r[u] * row_elems + chunk_el[u];
+      const uint32_t dst = stage_k + (uint32_t)((kWaveKeys * wave + 4 * u) * kHeadDim * 2);
+      lds_load16(kbase + off, dst);
+      lds_load16(vbase + off, dst + kVRegion);
     }
     if (bad) raise_status(a.status, PKV_STATUS_BAD_PAGE_ROW);
+    // everything older than those entries is tile n's rows, needed already
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWaitEntries) : "memory");
+    read_entries(n + kRowLead + 1);
   };
+  // End of a tile: this wavefront's rows of the next tile are in LDS and
+  // every LDS read of the current tile has returned; after the barrier every
+  // wavefront's rows are.
+  auto finish = [&]() __attribute__((always_inline)) {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kWaitRows) : "memory");
+  };
+
+  // per-lane LDS read addresses (bytes from the stage's K or V tile)
+  // K operand: row 32 mb + l32, logical chunk half + 2 jj ->
+  //   slot (2 jj) ^ (half ^ swz(l32 & 15)); row offset l32 * 256 + mb * 8192
+  uint32_t kaddr[8];
+  {
+    const int hk = half ^ swz(l32 & 15);
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) kaddr[jj] = (uint32_t)(l32 * 256 + (((2 * jj) ^ hk) << 4));
+  }
+  // V^T operand (transpose reads): in each 16-lane group lane j16 reads row
+  // key0 + j16 / 4 (and 8 rows on), logical elements nb * 32 + 16 ((l / 16) & 1)
+  // + 4 (j16 & 3); the XOR with 64 nb moves chunk 4 nb + b to its slot
+  uint32_t vaddr[2][4];
+  {
+    const int j16 = lane & 15;
+    const int b = ((lane >> 4) & 1) * 2 + ((j16 & 3) >> 1);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int r = 4 * half + (j16 >> 2) + 8 * p;
+      const int base = r * 256 + ((b ^ swz(r)) << 4) + 8 * (j16 & 1);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) vaddr[p][nb] = (uint32_t)(kVRegion + (base ^ (64 * nb)));
+    }
+  }
 
   f32x16 oacc[4];
 #pragma unroll
@@ -180,44 +290,29 @@ __global__ void __launch_bounds__(64 * kWaves, 8 / kWaves) extend_kernel(AttnArg
   // tiles whose keys all lie at or before the first row's position need no mask
   const int kt_mask = min(kv_end, ((min_pos + 1) / kKeyTile) * kKeyTile);
 
-  // tile kt from register set S into LDS stage S
-  auto store_tile = [&](int kt, auto set_tag) __attribute__((always_inline)) {
-    constexpr int S = decltype(set_tag)::value;
-    (void)kt;
-#pragma unroll
-    for (int u = 0; u < kLoads; ++u) {
-      const int key = kWaveKeys * wave + 4 * u + (lane >> 4);
-      *reinterpret_cast<uint4*>(&ks_all[S][key * kKsStride + (lane & 15) * 8]) = kpre[S][u];
-      *reinterpret_cast<uint4*>(&vs_all[S][key * kVsStride + (lane & 15) * 8]) = vpre[S][u];
-    }
-  };
-  // One 64-key tile in stage SET.  MASK: the tile reaches past the first
+  // One 64-key tile n in stage S.  MASK: the tile reaches past the first
   // row's position, so keys beyond a row's own position are masked (diagonal
   // and ragged end).
-  auto key_tile = [&](int kt, auto set_tag) __attribute__((always_inline)) {
-    constexpr int SET = decltype(set_tag)::value;
+  auto key_tile = [&](int n, auto stage_tag) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage_tag)::value;
+    const int kt = n * kKeyTile;
     const bool MASK = kt >= kt_mask;  // uniform
-    const uint16_t* ks = ks_all[SET];
-    const uint16_t* vs = vs_all[SET];
+    const uint8_t* ks = lds + S * kTileBytes;
+    const uint8_t* vs = lds + S * kTileBytes;  // vaddr holds the V region offset
 
     // S^T = K Q^T : two 32-key blocks (raw scores, scale folded into exp below);
     // the two accumulation chains alternate and the K operands are read from
-    // LDS four MFMAs ahead, the first four before the next tile's store and
-    // gathers.  sched_barrier pins that order: left to itself the compiler
-    // issued each read about one MFMA before its use and every MFMA waited
-    // for the LDS latency (3.7% of the launch on the shared-prefix batch).
+    // LDS four MFMAs ahead, the first four before the next tiles' loads are
+    // issued.  sched_barrier pins that order.
     f32x16 sacc[2];
     auto kread = [&](int j) __attribute__((always_inline)) {
-      return as_bf16x8(*reinterpret_cast<const uint4*>(&ks[((j & 1) * 32 + l32) * kKsStride + half * 8 + 16 * (j >> 1)]));
+      return as_bf16x8(*reinterpret_cast<const uint4*>(ks + kaddr[j >> 1] + (j & 1) * 8192));
     };
     bf16x8 kb[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) kb[j] = kread(j);
     __builtin_amdgcn_sched_barrier(0);
-    // the next tile goes to the other stage (last read before the previous
-    // barrier); its register set then receives the tile three ahead
-    store_tile(kt + kKeyTile, std::integral_constant<int, SET ^ 1>{});
-    gather(kt + 3 * kKeyTile, std::integral_constant<int, SET ^ 1>{});
+    issue(n);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -248,12 +343,11 @@ __global__ void __launch_bounds__(64 * kWaves, 8 / kWaves) extend_kernel(AttnArg
     // softmax, so their latency is hidden behind it.
     auto vread = [&](int m) __attribute__((always_inline)) {
       const int mb = m >> 3, kq = (m >> 2) & 1, nb = m & 3;
-      const int key0 = mb * 32 + 16 * kq + 4 * half;
-      const int j16 = lane & 15;
-      const uint16_t* vp = &vs[(key0 + (j16 >> 2)) * kVsStride + nb * 32 + ((lane >> 4) & 1) * 16 + 4 * (j16 & 3)];
-      const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)vp);
-      const v4s r2 =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(vp + 8 * kVsStride));
+      const int roff = mb * 8192 + kq * 4096;
+      const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)(vs + vaddr[0][nb] + roff));
+      const v4s r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)(vs + vaddr[1][nb] + roff));
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(r1, r2, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     bf16x8 vb[kVW];
@@ -310,27 +404,37 @@ __global__ void __launch_bounds__(64 * kWaves, 8 / kWaves) extend_kernel(AttnArg
       __builtin_amdgcn_sched_barrier(0);
     }
     lsum = lsum * alpha + (psum0 + psum1);
+    finish();
   };
 
+  // Prologue: the entries of tiles 0 .. 2, waited for together with the q
+  // rows (the empty asm statements use q here, so that the compiler's own
+  // wait for the q loads comes before the loop and not inside it), tile 0's
+  // entries into registers, then the issue steps of iterations -3 .. -1 (rows
+  // of tiles 0 .. 2); after the first barrier tile 0's rows are in LDS.
   load_entries(0);
-  gather(0, std::integral_constant<int, 0>{});
-  gather(kKeyTile, std::integral_constant<int, 1>{});
-  store_tile(0, std::integral_constant<int, 0>{});
-  gather(2 * kKeyTile, std::integral_constant<int, 0>{});
-  __syncthreads();
-  // both tiles of a pair always run, so every path into a tile has the same
-  // loads in flight (an odd last tile runs after the loop)
-  int kt = 0;
-  for (; kt + kKeyTile < kv_end; kt += 2 * kKeyTile) {
-    key_tile(kt, std::integral_constant<int, 0>{});
-    __syncthreads();
-    key_tile(kt + kKeyTile, std::integral_constant<int, 1>{});
-    __syncthreads();
+  load_entries(1);
+  load_entries(2);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) asm volatile("" ::"v"(qop[kk]));
+  read_entries(0);
+  issue(-3);
+  issue(-2);
+  issue(-1);
+  finish();
+  int n = 0;
+  for (; n + kStages <= n_kt; n += kStages) {
+    key_tile(n, std::integral_constant<int, 0>{});
+    key_tile(n + 1, std::integral_constant<int, 1>{});
+    key_tile(n + 2, std::integral_constant<int, 2>{});
+    key_tile(n + 3, std::integral_constant<int, 3>{});
   }
-  if (kt < kv_end) {
-    key_tile(kt, std::integral_constant<int, 0>{});
-    __syncthreads();
-  }
+  if (n < n_kt) key_tile(n, std::integral_constant<int, 0>{});
+  if (n + 1 < n_kt) key_tile(n + 1, std::integral_constant<int, 1>{});
+  if (n + 2 < n_kt) key_tile(n + 2, std::integral_constant<int, 2>{});
+  // no load may still be writing LDS when the workgroup ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   const float L = lsum + __shfl_xor(lsum, 32, 64);
   if (row_valid) {
