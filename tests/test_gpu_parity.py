@@ -310,6 +310,14 @@ def _edge_workloads():
     cases.append(("batch4096", build_workload("batch4096", 65, [RequestSpec(l, l + 1) for l in lens],
                                               num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=1,
                                               num_pool_rows=1 << 19, num_decode=4096)))
+    # extend items of 1 to 9 key tiles of 64 (the extend loop runs whole groups of four tiles, then up to
+    # three more one by one; every count of groups and leftover tiles), and a prefill whose items end
+    # at 64, 128, 192, 256 and 300 keys
+    spans = [(0, 1), (63, 1), (64, 1), (127, 2), (190, 3), (256, 1), (320, 20), (400, 30), (447, 65), (520, 10),
+             (0, 300)]
+    cases.append(("key_tiles", build_workload("key_tiles", 66, [RequestSpec(c, c + e) for c, e in spans],
+                                              num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=1,
+                                              num_pool_rows=1 << 14, num_decode=0)))
     # one long decode request spread over many splits, width exactly its length rounded to 32
     cases.append(("long_single", build_workload("long_single", 50, [RequestSpec(20000, 20001)],
                                                 num_qo_heads=64, num_kv_heads=8, head_dim=128, page_size=1,
