@@ -310,7 +310,7 @@ def measure(cfg, args, torch, flush_buf):
     has_decode = w.num_decode > 0
     has_extend = w.num_decode < w.num_reqs
 
-    # the calls of one step, in order; a batch of at most 512 new tokens does
+    # the calls of one step, in order; a batch of at most 1024 requests does
     # metadata and store in one launch (build_attn_metadata_store)
     if args.separate_store:
         calls = [("metadata", ds.metadata), ("kv_store", ds.store)]
@@ -409,8 +409,8 @@ def measure(cfg, args, torch, flush_buf):
     if "kv_store" in parts:
         out["store_gbps"] = round(st_bytes / (float(parts["kv_store"]) * 1e-3) / 1e9, 1)
     elif w.num_tokens > 512:
-        # the store of a large batch on its own (the step runs it inside
-        # build_attn_metadata_store); repeating it writes the same rows
+        # kv_store of a large batch on its own (the step stores inside the
+        # build_attn_metadata_store launch); repeating it writes the same rows
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
         torch.cuda.synchronize()
         for e0, e1 in evs:

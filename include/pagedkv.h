@@ -13,7 +13,7 @@
  *   paged_decode_attn    split-K decode attention (one new token per request)
  *   paged_extend_attn    chunked-prefill attention on a cached prefix
  * and around them:
- *   build_attn_metadata_store  the first two in one launch for small batches
+ *   build_attn_metadata_store  the first two in one launch (up to 1024 requests)
  *   paged_decode_attn_static   decode attention that allocates nothing
  *   kv_store_rope        kv_store with rotary position embedding (and an
  *                        optional per-head RMS norm) applied to q and k on
@@ -196,10 +196,10 @@ int build_attn_metadata(const pkv_batch* batch, const pkv_page_table* page_table
  * batch's new K/V rows at the out_loc rows it writes (the order the learning
  * notes' store_kv passage gives: rows are placed before attention reads
  * them), with identical results, in fewer launches: for a batch of at most
- * 512 new tokens and 1024 requests (every decode step of the configurations
- * here) one launch does both, its extra workgroups mapping 8 tokens each and
- * copying their rows while the first builds the metadata; larger batches
- * take the two calls' launches.  The pool's page_size and num_rows stand for
+ * 1024 requests (every configuration here) one launch does both, its extra
+ * workgroups mapping 8 tokens each and copying their rows while the first
+ * builds the metadata; larger batches take the two calls' launches.  The
+ * pool's page_size and num_rows stand for
  * build_attn_metadata's page_size and num_pool_rows, its num_kv_heads for
  * num_kv_heads.
  *   k_new, v_new : bf16 [num_tokens, Hkv, head_dim], contiguous, 16-byte aligned

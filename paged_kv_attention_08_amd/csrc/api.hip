@@ -168,7 +168,6 @@ int prepare_metadata(const pkv_batch* batch, const pkv_page_table* page_table, i
   a.status = meta->status;
   a.plan = static_cast<char*>(meta->plan);
   a.layout = L;
-  a.fuse_tokens = 0;
   a.pad_from = INT32_MAX;
   a.dummy_row = 0;
   a.pad_table_idx = a.pad_cached_len = a.pad_device_len = a.pad_alloc_rows = nullptr;
@@ -176,7 +175,7 @@ int prepare_metadata(const pkv_batch* batch, const pkv_page_table* page_table, i
   a.k_pool = a.v_pool = nullptr;
   a.store_stride_vec = 0;
   a.store_row_vec = 0;
-  a.store_blocks = 0;
+  a.map_blocks = 0;
   *out = a;
   return PKV_OK;
 }

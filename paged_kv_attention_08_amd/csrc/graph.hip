@@ -57,7 +57,7 @@ int enqueue_step(const pkv_decode_graph_desc& d, int32_t bs, MetaArgs* plan_args
   a.pad_device_len = d.device_len;
   a.pad_alloc_rows = d.alloc_rows;
   *plan_args = a;
-  // metadata and store (one kernel for up to 512 requests), then attention
+  // metadata and store (one kernel for up to 1024 requests), then attention
   hipError_t e = launch_metadata_store(a, st, s);
   if (e != hipSuccess) return hip_failed(e);
   return paged_decode_attn(&d.pool, &d.page_table, &b, &d.meta, d.q, d.o, d.num_qo_heads, d.sm_scale, d.workspace,

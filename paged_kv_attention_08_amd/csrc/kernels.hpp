@@ -77,7 +77,6 @@ struct MetaArgs {
   int32_t* status;
   char* plan;
   PlanLayout layout;
-  int32_t fuse_tokens;  // 1: plan_kernel also maps the tokens (small batches; see launch_metadata)
   // Graph-replay padding: requests [pad_from, B) are dummy requests (table row
   // dummy_row, cached_len 0, device_len 1, their new row the dummy page's row 0)
   // whatever the batch arrays hold; plan_kernel writes those values (and the
@@ -89,16 +88,18 @@ struct MetaArgs {
   int32_t* pad_cached_len;
   int32_t* pad_device_len;
   int32_t* pad_alloc_rows;
-  // Fused store (build_attn_metadata_store): when k_new is set and the batch
-  // is small enough for plan_kernel to map its tokens, workgroups 1..
-  // store_blocks of plan_kernel also copy the new K/V rows into the pool.
+  // Store in the metadata launch (build_attn_metadata_store): when k_new is
+  // set, the map blocks of plan_kernel also copy the new K/V rows into the
+  // pool.
   const uint4* k_new;
   const uint4* v_new;
   uint4* k_pool;
   uint4* v_pool;
   int64_t store_stride_vec;  // 16-byte vectors between pool rows
   int32_t store_row_vec;     // 16-byte vectors per K (or V) row of a token
-  int32_t store_blocks;      // set by the launcher
+  // workgroups 1..map_blocks of plan_kernel map the new tokens (0: a
+  // token_kernel launch does); set by the launcher
+  int32_t map_blocks;
 };
 
 struct AttnArgs {

@@ -8,20 +8,23 @@
 // guide", main line 3: the same quantities are seq_lens, extend_prefix_lens,
 // extend_seq_lens, req_pool_indices and out_cache_loc.
 //
-// Two launches on the caller's stream:
-//   plan_kernel  (one workgroup): per-request validation, running totals
-//                (qo_indptr, kv_indptr, last_indices, alloc offsets), the
-//                decode tile offsets and per-run share (the decode kernel
-//                splits the flat sequence of (request, group of KV heads, key
-//                tile) evenly over its runs) and the extend tile list,
-//                ordered by key count, most first (so the last workgroups to
-//                start are the shortest and the CUs finish together);
-//   token_kernel (one thread per new token): finds its request by binary
-//                search over qo_indptr and writes page_table, out_loc and
-//                positions.
-// For a small batch (at most kFuseTokens new tokens and kFuseReqs requests)
-// plan_kernel maps the tokens itself, from an LDS copy of qo_indptr, and the
-// second launch and the gap before it are saved.
+// One launch on the caller's stream, plan_kernel:
+//   workgroup 0: per-request validation, running totals (qo_indptr,
+//                kv_indptr, last_indices, alloc offsets), the decode tile
+//                offsets and per-run share (the decode kernel splits the flat
+//                sequence of (request, group of KV heads, key tile) evenly
+//                over its runs) and the extend tile list, ordered by key
+//                count, most first (so the last workgroups to start are the
+//                shortest and the CUs finish together);
+//   workgroups 1.. (map blocks, kMapTokens new tokens each): rebuild the two
+//                running totals they need in LDS, find each token's request
+//                by binary search and write page_table, out_loc and
+//                positions; with K/V given (build_attn_metadata_store) they
+//                also copy the tokens' K/V rows into the pool.
+// A batch of more than kFuseReqs requests (too many for the LDS copy of the
+// running totals) maps its tokens in a second launch instead, token_kernel
+// (one thread per new token, binary search over qo_indptr in memory), and is
+// stored by kv_store after it.
 // Inside a replayed decode graph the batch is padded here too (learning notes
 // graph passage: padding requests fill the batch up to the captured size and
 // point at the dummy page): requests from pad_from on are taken as dummy
@@ -38,9 +41,9 @@ constexpr int kPlanThreads = 256;
 constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kScanVals = 5;
 constexpr int kSortBuckets = 1024;  // extend tiles sorted by key count in steps of 64 keys (capped)
-constexpr int kFuseTokens = 512;    // new tokens plan_kernel maps itself
-constexpr int kFuseReqs = 1024;     // requests of such a batch (an LDS copy of qo_indptr)
-constexpr int kStoreTokens = 8;     // new tokens per store workgroup of a fused metadata + store launch
+constexpr int kFuseReqs = 1024;     // most requests whose running totals a map block copies to LDS
+constexpr int kMapTokens = 8;       // new tokens per map block
+constexpr int kCopyVec = 4;         // 16-byte K (and V) vectors a map-block thread loads before storing
 static_assert(kSortBuckets % kPlanThreads == 0, "whole buckets per thread");
 
 struct ReqInfo {
@@ -170,31 +173,33 @@ __device__ inline TokenRow token_row(const MetaArgs& a, int64_t t, const int32_t
   return out;
 }
 
-// Writes page_table, out_loc and positions of token t.  A token that gets no
-// row is marked -1 in out_loc and positions, so the store and RoPE calls skip
-// it instead of reusing a stale row.
-__device__ inline void map_token(const MetaArgs& a, int64_t t, const int32_t* qo, const int32_t* alloc_ptr) {
+// Writes page_table, out_loc and positions of token t and returns its row.  A
+// token that gets no row is marked -1 in out_loc and positions, so the store
+// and RoPE calls skip it instead of reusing a stale row.
+__device__ inline int32_t map_token(const MetaArgs& a, int64_t t, const int32_t* qo, const int32_t* alloc_ptr) {
   const TokenRow tr = token_row(a, t, qo, alloc_ptr);
   if (tr.bits) raise_status(a.status, tr.bits);
   if (tr.row < 0) {
     a.out_loc[t] = -1;
     a.positions[t] = -1;
-    return;
+    return -1;
   }
   a.page_table[(int64_t)tr.table_row * a.W + tr.j] = tr.row;
   a.out_loc[t] = tr.row;
   a.positions[t] = tr.j;
+  return tr.row;
 }
 
-// A store workgroup of the fused metadata + store launch (workgroups 1.. of
-// plan_kernel): it rebuilds the two running totals it needs (new tokens and
-// new pages per request) in LDS, maps its kStoreTokens tokens to rows as
-// map_token does and copies their K and V rows into the pool, consecutive
-// threads on consecutive 16-byte vectors of a row.  Workgroup 0 writes the
-// metadata meanwhile; the mapping here reads only page-table entries before
-// each request's cached_len, which workgroup 0 does not write.
-__device__ inline void store_block(const MetaArgs& a, int32_t* s_qo, int32_t* s_ap, int32_t (*smem)[kPlanWaves],
-                                   int32_t* s_rows) {
+// A map block (workgroups 1.. of plan_kernel): it rebuilds the two running
+// totals it needs (new tokens and new pages per request) in LDS, maps its
+// kMapTokens tokens as map_token does and, when K/V are given, copies their K
+// and V rows into the pool, consecutive threads on consecutive 16-byte
+// vectors of a row, each thread loading up to kCopyVec vectors of each before
+// storing them.  Workgroup 0 writes the plan meanwhile; the mapping reads only
+// page-table entries before each request's cached_len, which no workgroup of
+// the launch writes.
+__device__ inline void map_block(const MetaArgs& a, int32_t* s_qo, int32_t* s_ap, int32_t (*smem)[kPlanWaves],
+                                 int32_t* s_rows) {
   const int tid = threadIdx.x;
   int32_t carry_q = 0, carry_a = 0;
   if (tid == 0) {
@@ -216,24 +221,39 @@ __device__ inline void store_block(const MetaArgs& a, int32_t* s_qo, int32_t* s_
     carry_a += tot[1];
   }
   __syncthreads();
-  const int64_t t0 = (int64_t)(blockIdx.x - 1) * kStoreTokens;
-  if (tid < kStoreTokens) {
+  const int64_t t0 = (int64_t)(blockIdx.x - 1) * kMapTokens;
+  if (tid < kMapTokens) {
     const int64_t t = t0 + tid;
-    s_rows[tid] = t < a.T ? token_row(a, t, s_qo, s_ap).row : -1;
+    int32_t row = -1;
+    if (t < a.T) row = map_token(a, t, s_qo, s_ap);
+    s_rows[tid] = row;
   }
+  if (!a.k_new) return;
   __syncthreads();
   const int rv = a.store_row_vec;
-  for (int idx = tid; idx < kStoreTokens * rv; idx += kPlanThreads) {
-    const int k = idx / rv;
-    const int c = idx - k * rv;
-    const int32_t row = s_rows[k];
-    if (row < 0) continue;  // past the batch's tokens, or a token that got no row
-    const int64_t src = (t0 + k) * rv + c;
-    const uint4 kv = a.k_new[src];
-    const uint4 vv = a.v_new[src];
-    const int64_t dst = (int64_t)row * a.store_stride_vec + c;
-    a.k_pool[dst] = kv;
-    a.v_pool[dst] = vv;
+  const int n = kMapTokens * rv;
+  for (int base = 0; base < n; base += kCopyVec * kPlanThreads) {
+    uint4 kv[kCopyVec], vv[kCopyVec];
+    int64_t dst[kCopyVec];
+#pragma unroll
+    for (int q = 0; q < kCopyVec; ++q) {
+      const int idx = base + q * kPlanThreads + tid;
+      const int k = idx / rv;
+      const int c = idx - k * rv;
+      // -1: past the block's vectors, past the batch's tokens, or a token that got no row
+      const int32_t row = idx < n ? s_rows[min(k, kMapTokens - 1)] : -1;
+      const int64_t src = row >= 0 ? (t0 + k) * rv + c : 0;
+      kv[q] = row >= 0 ? a.k_new[src] : make_uint4(0, 0, 0, 0);
+      vv[q] = row >= 0 ? a.v_new[src] : make_uint4(0, 0, 0, 0);
+      dst[q] = row >= 0 ? (int64_t)row * a.store_stride_vec + c : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < kCopyVec; ++q) {
+      if (dst[q] >= 0) {
+        a.k_pool[dst[q]] = kv[q];
+        a.v_pool[dst[q]] = vv[q];
+      }
+    }
   }
 }
 
@@ -245,11 +265,11 @@ __global__ void __launch_bounds__(256) token_kernel(MetaArgs a) {
 
 __global__ void __launch_bounds__(kPlanThreads) plan_kernel(MetaArgs a) {
   __shared__ int32_t smem[kScanVals][kPlanWaves];
-  __shared__ int32_t s_qo[kFuseReqs + 1];  // qo_indptr of a fused batch
-  if (blockIdx.x > 0) {  // a store workgroup (uniform for the workgroup)
+  if (blockIdx.x > 0) {  // a map block (uniform for the workgroup)
+    __shared__ int32_t s_qo[kFuseReqs + 1];
     __shared__ int32_t s_ap[kFuseReqs + 1];
-    __shared__ int32_t s_rows[kStoreTokens];
-    store_block(a, s_qo, s_ap, smem, s_rows);
+    __shared__ int32_t s_rows[kMapTokens];
+    map_block(a, s_qo, s_ap, smem, s_rows);
     return;
   }
   const int tid = threadIdx.x;
@@ -269,7 +289,6 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(MetaArgs a) {
     a.kv_indptr[0] = 0;
     dec_tile_ptr[0] = 0;
     alloc_ptr[0] = 0;
-    s_qo[0] = 0;
   }
   for (int base = 0; base < a.B; base += kPlanThreads) {
     const int i = base + tid;
@@ -296,12 +315,11 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(MetaArgs a) {
     if (i < a.B) {
       const int32_t qo_end = carry[0] + ex[0] + ri.ext;
       a.qo_indptr[i + 1] = qo_end;
-      if (a.fuse_tokens) s_qo[i + 1] = qo_end;
       a.kv_indptr[i + 1] = carry[1] + ex[1] + ri.dl;
       a.last_indices[i] = qo_end - 1;
       alloc_ptr[i + 1] = carry[2] + ex[2] + ri.new_pages;
-      // a padding request's one new page is the dummy page (for token_kernel,
-      // which reads it from alloc_rows; the fused mapping below knows it)
+      // a padding request's one new page is the dummy page (its alloc entry,
+      // for readers of alloc_rows; the token mapping knows it anyway)
       if (i >= a.pad_from && carry[2] + ex[2] < a.num_alloc) a.pad_alloc_rows[carry[2] + ex[2]] = 0;
       dec_tile_ptr[i + 1] = carry[3] + ex[3] + ri.dtiles;
       const int32_t tb = carry[4] + ex[4];
@@ -376,18 +394,11 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(MetaArgs a) {
       tiles[atomicAdd(&bucket[tile_bucket(tt)], 1)] = tt;
     }
   }
-  if (a.fuse_tokens) {
-    // the alloc offsets other threads wrote to global memory, and s_qo
-    __threadfence_block();
-    __syncthreads();
-    for (int64_t t = tid; t < a.T; t += kPlanThreads) map_token(a, t, s_qo, alloc_ptr);
-  }
 }
 
 MetaArgs metadata_launch_args(const MetaArgs& a_in) {
   MetaArgs a = a_in;
-  a.fuse_tokens = (a.T <= kFuseTokens && a.B <= kFuseReqs) ? 1 : 0;
-  a.store_blocks = (a.k_new && a.fuse_tokens && a.T > 0) ? (int32_t)((a.T + kStoreTokens - 1) / kStoreTokens) : 0;
+  a.map_blocks = (a.B <= kFuseReqs && a.T > 0) ? (int32_t)((a.T + kMapTokens - 1) / kMapTokens) : 0;
   return a;
 }
 
@@ -395,21 +406,21 @@ MetaArgs metadata_launch_args(const MetaArgs& a_in) {
 
 hipError_t launch_metadata(const MetaArgs& a_in, hipStream_t s) {
   const MetaArgs a = metadata_launch_args(a_in);
-  hipLaunchKernelGGL(plan_kernel, dim3(1 + a.store_blocks), dim3(kPlanThreads), 0, s, a);
+  hipLaunchKernelGGL(plan_kernel, dim3(1 + a.map_blocks), dim3(kPlanThreads), 0, s, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.T == 0 || a.fuse_tokens) return e;
+  if (e != hipSuccess || a.T == 0 || a.map_blocks > 0) return e;
   const int64_t blocks = (a.T + 255) / 256;
   hipLaunchKernelGGL(token_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-bool metadata_stores_rows(const MetaArgs& a) { return metadata_launch_args(a).store_blocks > 0; }
+bool metadata_stores_rows(const MetaArgs& a) { return a.k_new && metadata_launch_args(a).map_blocks > 0; }
 
 void metadata_plan_node(const MetaArgs& a, MetaArgs* args, void** argv, hipKernelNodeParams* p) {
   *args = metadata_launch_args(a);
   argv[0] = args;
   p->func = reinterpret_cast<void*>(plan_kernel);
-  p->gridDim = dim3(1 + args->store_blocks);
+  p->gridDim = dim3(1 + args->map_blocks);
   p->blockDim = dim3(kPlanThreads);
   p->sharedMemBytes = 0;
   p->kernelParams = argv;

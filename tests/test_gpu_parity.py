@@ -62,9 +62,9 @@ def test_small_config(cfg):
     ds.free()
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
-def test_full_config(cfg):
-    w = configs.FULL[cfg]()
+def full_samples(cfg, w):
+    """Decode requests and extend tokens of a full-size workload that the
+    oracle checks one by one (None: all of them)."""
     dec = None
     if w.num_decode > 64:
         rng = np.random.default_rng(cfg)
@@ -72,6 +72,13 @@ def test_full_config(cfg):
     elif cfg == 4:
         dec = [0, 7, 15, 31]
     ext = P.sample_tokens(w, per_request=6, seed=cfg) if w.num_decode < w.num_reqs else None
+    return dec, ext
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_full_config(cfg):
+    w = configs.FULL[cfg]()
+    dec, ext = full_samples(cfg, w)
     ds, _, _ = run_case(w, decode_requests=dec, extend_tokens=ext, label=f"full{cfg}")
     ds.free()
 
@@ -292,8 +299,9 @@ def _edge_workloads():
                                                       new_tokens=150, num_pool_rows=64 * 64,
                                                       page_order="sequential")))
     # batches at the size where build_attn_metadata stops mapping the tokens inside its
-    # one-workgroup plan kernel (512 new tokens) and launches a kernel for them
-    for nreq in (512, 513):
+    # plan launch (1024 requests: the LDS copy of the running totals) and launches a
+    # kernel for them, and at the earlier threshold of 512 new tokens
+    for nreq in (512, 513, 1024, 1025):
         lens = [(37 * k) % 300 + 1 for k in range(nreq)]
         reqs = [RequestSpec(l, l + 1) for l in lens]
         cases.append((f"meta{nreq}", build_workload(f"meta{nreq}", 62 + nreq % 2, reqs, num_qo_heads=32,
@@ -351,21 +359,24 @@ def test_empty_batch():
     ds.free()
 
 
-FUSED_CASES = ["small1", "small2", "small3", "small4", "small5", "full1", "full2", "single_key", "group16", "kv3",
-               "page2", "page16", "page32", "seq_pages64", "meta512", "meta513", "batch4096"]
+FUSED_CASES = ["small1", "small2", "small3", "small4", "small5", "full1", "full2", "full3", "full5", "single_key",
+               "group16", "kv3", "page2", "page16", "page32", "seq_pages64", "meta512", "meta513", "meta1024",
+               "meta1025", "batch4096"]
 
 
 @pytest.mark.parametrize("name", FUSED_CASES)
 def test_metadata_and_store_in_one_call(name):
     """build_attn_metadata_store gives what build_attn_metadata + kv_store give:
     the same bit-exact metadata, stored rows and untouched pool, and outputs
-    within the bar (one launch up to 512 new tokens: meta512; two above:
-    meta513)."""
+    within the bar (one launch up to 1024 requests, any number of new tokens:
+    meta1024, full3; two above: meta1025, batch4096)."""
+    ext = None
     if name.startswith("small"):
         w = configs.small(int(name[5:]))
     elif name.startswith("full"):
         w = configs.FULL[int(name[4:])]()
+        _, ext = full_samples(int(name[4:]), w)  # every decode request, sampled extend tokens
     else:
         w = dict(_edge_workloads())[name]
-    ds, _, _ = run_case(w, label=f"fused {name}", fused_store=True)
+    ds, _, _ = run_case(w, extend_tokens=ext, label=f"fused {name}", fused_store=True)
     ds.free()
