@@ -130,11 +130,13 @@ def cpu_baseline(w, kind: str, budget_s: float):
 
 def graph_measurement(ds, w, args, stream):
     """The decode step (metadata, store, decode attention) replayed as one HIP
-    graph captured for this batch size, against the same three calls issued
-    eagerly; per-step time from events around K back-to-back steps (host
-    launch cost included: what a graph saves).  Replays with one real-request
-    count throughout, and with a count that changes on every replay (the
-    graph's first kernel node then gets new arguments each time)."""
+    graph captured for this batch size, against the same calls issued
+    eagerly, through the plain binding and as calls bound once (bind_*);
+    per-step time from events around K back-to-back steps (host launch cost
+    included: what a graph or a bound call saves).  Replays with one
+    real-request count throughout, and with a count that changes on every
+    replay (the graph's first kernel node then gets new arguments each
+    time)."""
     import torch
     import paged_kv_attention_08_amd as pkv
 
@@ -168,8 +170,19 @@ def graph_measurement(ds, w, args, stream):
                 ds.metadata_store(side)
             ds.decode(side)
 
+        bb = pkv.BoundBatch(ds.batch)
+        bound = [pkv.bind_build_attn_metadata_store(bb, ds.page_table, ds.pool, ds.alloc_rows, w.num_qo_heads,
+                                                    ds.meta, ds.k_new, ds.v_new, stream=side),
+                 pkv.bind_paged_decode_attn(ds.pool, ds.page_table, bb, ds.meta, ds.q, ds.o, w.sm_scale,
+                                            ds.workspace, stream=side)]
+
+        def eager_bound(k):
+            for call in bound:
+                call()
+
         n = w.num_reqs
         eager_ms = timed(eager)
+        bound_ms = timed(eager_bound)
         graph_ms = timed(lambda k: graph.replay(n, stream=side))
         graph_var_ms = timed(lambda k: graph.replay(n - (k & 1), stream=side)) if n > 1 else graph_ms
     finally:
@@ -179,9 +192,10 @@ def graph_measurement(ds, w, args, stream):
             t.copy_(v)  # padding written into the last slot by the changing-count replays
         torch.cuda.synchronize()
     assert ds.status() == 0, f"device status {ds.status():#x}"
-    return {"batch": w.num_reqs, "eager_step_ms": round(eager_ms, 4), "graph_step_ms": round(graph_ms, 4),
-            "graph_step_ms_count_changing": round(graph_var_ms, 4),
-            "what": "metadata + store + paged_decode_attn, eager calls vs one graph replay"}
+    return {"batch": w.num_reqs, "eager_step_ms": round(eager_ms, 4), "eager_bound_step_ms": round(bound_ms, 4),
+            "graph_step_ms": round(graph_ms, 4), "graph_step_ms_count_changing": round(graph_var_ms, 4),
+            "what": "metadata + store + paged_decode_attn: eager calls through the binding, eager calls bound "
+                    "once, one graph replay"}
 
 
 def alloc_measurement(ds, w, args, stream):

@@ -26,6 +26,8 @@ __all__ = ["PagedKVError", "KVPoolTensors", "KVCacheTensors", "BatchTensors", "M
            "build_attn_metadata_store",
            "paged_decode_attn", "paged_decode_attn_static", "paged_extend_attn", "plan_bytes", "workspace_bytes", "library_path", "plan_view",
            "rope_cos_sin_cache", "kv_store_rope", "PKV_STATUS_BAD_POSITION", "DecodeGraph", "PageFreeList",
+           "BoundBatch", "BoundCall", "bind_kv_store", "bind_build_attn_metadata", "bind_build_attn_metadata_store",
+           "bind_paged_decode_attn", "bind_paged_extend_attn",
            "PKV_STATUS_OUT_OF_PAGES", "PKV_STATUS_FREE_OVERFLOW",
            "PKV_STATUS_BAD_ALLOC", "PKV_STATUS_BAD_DECODE", "PKV_STATUS_BAD_LENGTHS", "PKV_STATUS_BAD_OUT_LOC",
            "PKV_STATUS_BAD_PAGE_ROW", "PKV_STATUS_BAD_TABLE_IDX", "PKV_STATUS_TOKEN_COUNT"]
@@ -210,8 +212,7 @@ def workspace_bytes(max_reqs: int, num_qo_heads: int, head_dim: int = 128) -> in
     return n
 
 
-def kv_store(pool: KVPoolTensors, k_new: torch.Tensor, v_new: torch.Tensor, out_loc: torch.Tensor,
-             status: Optional[torch.Tensor] = None, stream=None) -> None:
+def _kv_store_args(pool, k_new, v_new, out_loc, status):
     p = pool.struct()
     _need(k_new, "k_new", torch.bfloat16, 3)
     _need(v_new, "v_new", torch.bfloat16, 3)
@@ -221,29 +222,37 @@ def kv_store(pool: KVPoolTensors, k_new: torch.Tensor, v_new: torch.Tensor, out_
         raise ValueError("k_new / v_new / out_loc shapes do not match the pool")
     if status is not None:
         _need(status, "status", torch.int32, 1)
-    _check("kv_store", _lib.lib().kv_store(ctypes.byref(p), k_new.data_ptr(), v_new.data_ptr(), out_loc.data_ptr(),
-                                           t, _ptr(status), _stream(stream)))
+    return (ctypes.byref(p), k_new.data_ptr(), v_new.data_ptr(), out_loc.data_ptr(), t, _ptr(status)), (p,)
+
+
+def kv_store(pool: KVPoolTensors, k_new: torch.Tensor, v_new: torch.Tensor, out_loc: torch.Tensor,
+             status: Optional[torch.Tensor] = None, stream=None) -> None:
+    args, _keep = _kv_store_args(pool, k_new, v_new, out_loc, status)
+    _check("kv_store", _lib.lib().kv_store(*args, _stream(stream)))
+
+
+def _metadata_args(batch, page_table, page_size, num_pool_rows, alloc_rows, num_qo_heads, num_kv_heads, meta):
+    b = batch.struct()
+    _need(page_table, "page_table", torch.int32, 2)
+    _need(alloc_rows, "alloc_rows", torch.int32, 1)
+    if meta.out_loc.numel() < batch.num_tokens or meta.positions.numel() < batch.num_tokens:
+        raise ValueError("out_loc / positions hold fewer entries than the batch's new tokens")
+    pt = _lib.PageTable(page_table.data_ptr(), page_table.shape[0], page_table.shape[1])
+    m = meta.struct()
+    return (ctypes.byref(b), ctypes.byref(pt), page_size, num_pool_rows,
+            alloc_rows.data_ptr() if alloc_rows.numel() else None, alloc_rows.numel(), num_qo_heads, num_kv_heads,
+            ctypes.byref(m)), (b, pt, m)
 
 
 def build_attn_metadata(batch: BatchTensors, page_table: torch.Tensor, page_size: int, num_pool_rows: int,
                         alloc_rows: torch.Tensor, num_qo_heads: int, num_kv_heads: int, meta: MetadataBuffers,
                         stream=None) -> None:
-    b = batch.struct()
-    _need(page_table, "page_table", torch.int32, 2)
-    _need(alloc_rows, "alloc_rows", torch.int32, 1)
-    pt = _lib.PageTable(page_table.data_ptr(), page_table.shape[0], page_table.shape[1])
-    m = meta.struct()
-    _check("build_attn_metadata",
-           _lib.lib().build_attn_metadata(ctypes.byref(b), ctypes.byref(pt), page_size, num_pool_rows,
-                                          alloc_rows.data_ptr() if alloc_rows.numel() else None, alloc_rows.numel(),
-                                          num_qo_heads, num_kv_heads, ctypes.byref(m), _stream(stream)))
+    args, _keep = _metadata_args(batch, page_table, page_size, num_pool_rows, alloc_rows, num_qo_heads,
+                                 num_kv_heads, meta)
+    _check("build_attn_metadata", _lib.lib().build_attn_metadata(*args, _stream(stream)))
 
 
-def build_attn_metadata_store(batch: BatchTensors, page_table: torch.Tensor, pool: KVPoolTensors,
-                              alloc_rows: torch.Tensor, num_qo_heads: int, meta: MetadataBuffers, k_new: torch.Tensor,
-                              v_new: torch.Tensor, stream=None) -> None:
-    """build_attn_metadata followed by kv_store of k_new / v_new at the
-    out_loc rows it writes, in one launch for small batches."""
+def _metadata_store_args(batch, page_table, pool, alloc_rows, num_qo_heads, meta, k_new, v_new):
     b = batch.struct()
     p = pool.struct()
     _need(page_table, "page_table", torch.int32, 2)
@@ -252,16 +261,24 @@ def build_attn_metadata_store(batch: BatchTensors, page_table: torch.Tensor, poo
     _need(v_new, "v_new", torch.bfloat16, 3)
     if v_new.shape != k_new.shape or k_new.shape[1:] != pool.k.shape[1:] or k_new.shape[0] < batch.num_tokens:
         raise ValueError("k_new / v_new shapes do not match the batch and pool")
+    if meta.out_loc.numel() < batch.num_tokens or meta.positions.numel() < batch.num_tokens:
+        raise ValueError("out_loc / positions hold fewer entries than the batch's new tokens")
     pt = _lib.PageTable(page_table.data_ptr(), page_table.shape[0], page_table.shape[1])
     m = meta.struct()
-    _check("build_attn_metadata_store",
-           _lib.lib().build_attn_metadata_store(ctypes.byref(b), ctypes.byref(pt), ctypes.byref(p),
-                                                alloc_rows.data_ptr() if alloc_rows.numel() else None,
-                                                alloc_rows.numel(), num_qo_heads, ctypes.byref(m), k_new.data_ptr(),
-                                                v_new.data_ptr(), _stream(stream)))
+    return (ctypes.byref(b), ctypes.byref(pt), ctypes.byref(p), alloc_rows.data_ptr() if alloc_rows.numel() else None,
+            alloc_rows.numel(), num_qo_heads, ctypes.byref(m), k_new.data_ptr(), v_new.data_ptr()), (b, pt, p, m)
 
 
-def _attn(fn_name, pool, page_table, batch, meta, q, o, sm_scale, workspace, stream):
+def build_attn_metadata_store(batch: BatchTensors, page_table: torch.Tensor, pool: KVPoolTensors,
+                              alloc_rows: torch.Tensor, num_qo_heads: int, meta: MetadataBuffers, k_new: torch.Tensor,
+                              v_new: torch.Tensor, stream=None) -> None:
+    """build_attn_metadata followed by kv_store of k_new / v_new at the
+    out_loc rows it writes, in one launch for batches of up to 1024 requests."""
+    args, _keep = _metadata_store_args(batch, page_table, pool, alloc_rows, num_qo_heads, meta, k_new, v_new)
+    _check("build_attn_metadata_store", _lib.lib().build_attn_metadata_store(*args, _stream(stream)))
+
+
+def _attn_args(pool, page_table, batch, meta, q, o, sm_scale, workspace):
     p = pool.struct()
     b = batch.struct()
     _need(page_table, "page_table", torch.int32, 2)
@@ -275,9 +292,13 @@ def _attn(fn_name, pool, page_table, batch, meta, q, o, sm_scale, workspace, str
     if workspace is not None:
         _need(workspace, "workspace", workspace.dtype, 1)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    fn = getattr(_lib.lib(), fn_name)
-    _check(fn_name, fn(ctypes.byref(p), ctypes.byref(pt), ctypes.byref(b), ctypes.byref(m), q.data_ptr(),
-                       o.data_ptr(), q.shape[1], float(sm_scale), ws_ptr, ws_bytes, _stream(stream)))
+    return (ctypes.byref(p), ctypes.byref(pt), ctypes.byref(b), ctypes.byref(m), q.data_ptr(), o.data_ptr(),
+            q.shape[1], float(sm_scale), ws_ptr, ws_bytes), (p, pt, b, m)
+
+
+def _attn(fn_name, pool, page_table, batch, meta, q, o, sm_scale, workspace, stream):
+    args, _keep = _attn_args(pool, page_table, batch, meta, q, o, sm_scale, workspace)
+    _check(fn_name, getattr(_lib.lib(), fn_name)(*args, _stream(stream)))
 
 
 def paged_decode_attn(pool: KVPoolTensors, page_table: torch.Tensor, batch: BatchTensors, meta: MetadataBuffers,
@@ -356,6 +377,112 @@ def kv_store_rope(pool: KVPoolTensors, q: torch.Tensor, k_new: torch.Tensor, v_n
         ctypes.byref(p), q.data_ptr(), q.shape[1], k_new.data_ptr(), v_new.data_ptr(), out_loc.data_ptr(),
         positions.data_ptr(), t, cos_sin_cache.data_ptr(), cos_sin_cache.shape[0],
         ctypes.byref(norm) if norm is not None else None, _ptr(status), _stream(stream)))
+
+
+class BoundBatch:
+    """A batch whose C struct is built once and shared by every call bound to
+    it (bind_*): set_counts changes the request and token counts all of them
+    see.  max_tokens (default: the batch's num_tokens) is the most new tokens
+    a later set_counts may give; the bound calls' token buffers are checked
+    against it when they are bound."""
+
+    def __init__(self, batch: BatchTensors, max_tokens: Optional[int] = None):
+        self.batch = batch
+        self._struct = batch.struct()
+        self.max_reqs = batch.table_idx.numel()
+        self.max_tokens = batch.num_tokens if max_tokens is None else int(max_tokens)
+        if self.max_tokens < batch.num_tokens:
+            raise ValueError("max_tokens below the batch's num_tokens")
+
+    def struct(self) -> _lib.Batch:
+        return self._struct
+
+    @property
+    def num_tokens(self) -> int:
+        """The token capacity bound calls' buffers must hold."""
+        return self.max_tokens
+
+    def set_counts(self, num_reqs: int, num_decode: int, num_tokens: int) -> None:
+        """Requests [0, num_reqs) of the batch arrays, the first num_decode of
+        them decode requests, with num_tokens new tokens in all."""
+        if not (0 <= num_decode <= num_reqs <= self.max_reqs and 0 <= num_tokens <= self.max_tokens):
+            raise ValueError(f"counts ({num_reqs}, {num_decode}, {num_tokens}) outside the bound batch "
+                             f"({self.max_reqs} requests, {self.max_tokens} tokens)")
+        s = self._struct
+        s.num_reqs = num_reqs
+        s.num_decode = num_decode
+        s.num_tokens = num_tokens
+
+
+class BoundCall:
+    """One library call with its arguments checked and marshalled once.
+    Calling it launches the call again on the bound stream (or the stream
+    given): the buffers' contents may change between calls, their addresses
+    may not (the bound call keeps the tensors alive), and the batch counts
+    change through the BoundBatch it was bound to.  Per call it costs one
+    ctypes call, against about 9 us of Python argument checks for the plain
+    functions, so back-to-back eager steps of a small batch are bound by the
+    GPU rather than by the host."""
+    __slots__ = ("name", "_fn", "_args", "_stream", "_keep")
+
+    def __init__(self, name, args, keep, stream):
+        self.name = name
+        self._fn = getattr(_lib.lib(), name)
+        self._args = args
+        self._keep = keep
+        self._stream = _stream(stream)
+
+    def __call__(self, stream=None) -> None:
+        code = self._fn(*self._args, self._stream if stream is None else _stream(stream))
+        if code != _lib.PKV_OK:
+            raise PagedKVError(self.name, code)
+
+
+def _bound_refs(*objs):
+    return tuple(x for x in objs if x is not None)
+
+
+def bind_kv_store(pool: KVPoolTensors, k_new: torch.Tensor, v_new: torch.Tensor, out_loc: torch.Tensor,
+                  status: Optional[torch.Tensor] = None, stream=None) -> BoundCall:
+    """kv_store bound once (see BoundCall); stores all k_new.shape[0] rows."""
+    args, keep = _kv_store_args(pool, k_new, v_new, out_loc, status)
+    return BoundCall("kv_store", args, keep + _bound_refs(pool, k_new, v_new, out_loc, status), stream)
+
+
+def bind_build_attn_metadata(batch: BoundBatch, page_table: torch.Tensor, page_size: int, num_pool_rows: int,
+                             alloc_rows: torch.Tensor, num_qo_heads: int, num_kv_heads: int, meta: MetadataBuffers,
+                             stream=None) -> BoundCall:
+    """build_attn_metadata bound once (see BoundCall)."""
+    args, keep = _metadata_args(batch, page_table, page_size, num_pool_rows, alloc_rows, num_qo_heads,
+                                num_kv_heads, meta)
+    return BoundCall("build_attn_metadata", args, keep + _bound_refs(batch, page_table, alloc_rows, meta), stream)
+
+
+def bind_build_attn_metadata_store(batch: BoundBatch, page_table: torch.Tensor, pool: KVPoolTensors,
+                                   alloc_rows: torch.Tensor, num_qo_heads: int, meta: MetadataBuffers,
+                                   k_new: torch.Tensor, v_new: torch.Tensor, stream=None) -> BoundCall:
+    """build_attn_metadata_store bound once (see BoundCall)."""
+    args, keep = _metadata_store_args(batch, page_table, pool, alloc_rows, num_qo_heads, meta, k_new, v_new)
+    return BoundCall("build_attn_metadata_store", args,
+                     keep + _bound_refs(batch, page_table, pool, alloc_rows, meta, k_new, v_new), stream)
+
+
+def bind_paged_decode_attn(pool: KVPoolTensors, page_table: torch.Tensor, batch: BoundBatch, meta: MetadataBuffers,
+                           q: torch.Tensor, o: torch.Tensor, sm_scale: float, workspace: torch.Tensor,
+                           stream=None) -> BoundCall:
+    """paged_decode_attn bound once (see BoundCall)."""
+    args, keep = _attn_args(pool, page_table, batch, meta, q, o, sm_scale, workspace)
+    return BoundCall("paged_decode_attn", args, keep + _bound_refs(pool, page_table, batch, meta, q, o, workspace),
+                     stream)
+
+
+def bind_paged_extend_attn(pool: KVPoolTensors, page_table: torch.Tensor, batch: BoundBatch, meta: MetadataBuffers,
+                           q: torch.Tensor, o: torch.Tensor, sm_scale: float,
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> BoundCall:
+    """paged_extend_attn bound once (see BoundCall)."""
+    args, keep = _attn_args(pool, page_table, batch, meta, q, o, sm_scale, workspace)
+    return BoundCall("paged_extend_attn", args, keep + _bound_refs(pool, page_table, batch, meta, q, o, workspace),
+                     stream)
 
 
 class DecodeGraph:
