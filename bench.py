@@ -469,8 +469,8 @@ def measure(cfg, args, torch, flush_buf):
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="after the warm-up steps, untimed steps for at least this long (clock ramp)")
     ap.add_argument("--configs", default=DEFAULT_CONFIGS,
