@@ -27,6 +27,17 @@ REL_MAX_TOL = 1e-2   # max|d| / max|o_ref| over the compared outputs
 ROW_REL_TOL = 2e-2   # per (token, query head): max over dims of |d| / max over dims of |o_ref|
 
 
+def widen_scores(w, factor: float):
+    """Scale every q and K value of the workload by factor (rounded back to
+    bf16), in place: the scores grow by factor^2, so the softmax of each row
+    concentrates on a few keys.  V is left as drawn."""
+    from workloads.synth import bf16_bits_to_float32, float32_to_bf16_bits
+    for name in ("q", "k_new", "k_cached"):
+        a = getattr(w, name)
+        setattr(w, name, float32_to_bf16_bits(bf16_bits_to_float32(a) * np.float32(factor)))
+    return w
+
+
 def sample_tokens(w, per_request: int = 12, seed: int = 0):
     """Chunk offsets to check per extend request: both ends, the edges of
     tiles of 16..256 tokens, random."""

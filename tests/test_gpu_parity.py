@@ -55,6 +55,16 @@ def run_case(w, decode_requests=None, extend_tokens=None, label="", fused_store=
     return ds, ref, stats
 
 
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_wide_scores(cfg):
+    """q and K at 3 times N(0, 1): scores with a standard deviation near 9, so
+    each softmax row sits on a few keys and the rounding of the score scaling
+    shows (tests/test_parity_sensitivity.py: the bar passes fp32 scaling and
+    fails q * scale rounded to bf16 at this spread)."""
+    w = P.widen_scores(configs.small(cfg), 3.0)
+    run_case(w, label=f"wide-scores-{cfg}")
+
+
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_small_config(cfg):
     w = configs.small(cfg)

@@ -9,7 +9,9 @@ dim 128, contexts drawn from the long-decode range), the fp64 oracle's own
 output rounded to bf16 (what a correct kernel returns at best) must pass the
 whole bar with a wide margin, while the oracle run with one 32-key tile
 removed from, or repeated in, a request's page-table row at the start, middle
-or end of the context must fail it.  Nothing here touches the GPU path.
+or end of the context must fail it.  A second group of checks, at a wide
+score spread, shows the same bar separating the kernels' fp32 score scaling
+from a cheaper bf16 one.  Nothing here touches the GPU path.
 """
 import numpy as np
 import pytest
@@ -85,3 +87,73 @@ def test_lost_or_doubled_tile_fails_the_bar(long_case, mode, where):
         # ... both relative bounds do not
         assert stats["rel_max"] > P.REL_MAX_TOL and stats["row_rel_max"] > P.ROW_REL_TOL, stats
         assert P.bar_failures(stats)
+
+
+# ---------------------------------------------------------------------------
+# Wide score spread.  With q and K at 3 times N(0, 1) (scores with a standard
+# deviation of about 9, so a row's softmax sits on a few keys), the bar must
+# still hold for the arithmetic the kernels use, scores in fp32 scaled by
+# scale * log2(e) in fp32 and exponentiated against the row max, probabilities
+# rounded to bf16 for the PV product, and must fail the shortcut of folding
+# scale * log2(e) into q before the QK^T product (q * scale rounded to bf16).
+# The two are emulated here in numpy on the oracle's own gathered rows: this
+# pins what the wide-score GPU parity cases can see.  Softmax as defined in the
+# mini-sglang architecture deep dive, section 5.2 (FlashAttention).
+# ---------------------------------------------------------------------------
+
+WIDE = 3.0
+
+
+def _round_bf16(x):
+    return bf16_bits_to_float32(float32_to_bf16_bits(np.asarray(x, dtype=np.float32)))
+
+
+def _emulated_row(q, K, V, scale, fold_scale_into_q):
+    c = np.float32(scale * np.log2(np.e))
+    q32, K32 = q.astype(np.float32), K.astype(np.float32)
+    s = (_round_bf16(q32 * c) @ K32.T) if fold_scale_into_q else (q32 @ K32.T) * c
+    p = _round_bf16(np.exp2(s - s.max())).astype(np.float64)
+    return (p @ V) / p.sum()
+
+
+@pytest.fixture(scope="module")
+def wide_case():
+    w = P.widen_scores(configs.small(2, seed=7), WIDE)
+    return w, reference_step(w)
+
+
+def _emulated_outputs(w, ref, fold):
+    pt = ref["meta"]["page_table"]
+    G = w.num_qo_heads // w.num_kv_heads
+    got, want = [], []
+    for i in range(w.num_reqs):
+        if w.is_padding[i]:
+            continue
+        rows = O.gather_rows(pt, int(w.table_idx[i]), int(w.device_len[i]))
+        K, V = ref["pool"].gather(rows)
+        q = O.widen_bf16(w.q[i])  # decode: request i's one new token is token i
+        got.append(as_bf16(np.stack([_emulated_row(q[h], K[:, h // G], V[:, h // G], w.sm_scale, fold)
+                                     for h in range(w.num_qo_heads)])))
+        want.append(ref["out"][i])
+    return np.stack(got), np.stack(want)
+
+
+def test_wide_scores_are_peaked(wide_case):
+    w, ref = wide_case
+    q = O.widen_bf16(w.q[0, 0])
+    rows = O.gather_rows(ref["meta"]["page_table"], int(w.table_idx[0]), int(w.device_len[0]))
+    K, _ = ref["pool"].gather(rows)
+    s = K[:, 0, :] @ q * w.sm_scale
+    assert s.std() > 6.0  # about 9: a few keys carry each row
+
+
+def test_wide_scores_fp32_scaling_passes(wide_case):
+    w, ref = wide_case
+    stats = P.attention_error_stats(*_emulated_outputs(w, ref, fold=False))
+    assert not P.bar_failures(stats), stats
+
+
+def test_wide_scores_scale_folded_into_q_fails(wide_case):
+    w, ref = wide_case
+    stats = P.attention_error_stats(*_emulated_outputs(w, ref, fold=True))
+    assert P.bar_failures(stats), stats
