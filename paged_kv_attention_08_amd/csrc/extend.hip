@@ -323,11 +323,14 @@ __global__ void __launch_bounds__(64 * kWaves, 8 / kWaves) extend_kernel(AttnArg
     }
     // element v of block mb is key kt + 32 mb + 8 (v / 4) + 4 half + v % 4 of row l32
     if (MASK) {
+      // key kt + 4 half + k_off > pos  <=>  k_off > pos - kt - 4 half: one
+      // subtraction per lane, then a compare against a constant per element
+      const int lim = pos - kt - 4 * half;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int v = 0; v < 16; ++v)
-          if (kt + 32 * mb + 8 * (v >> 2) + 4 * half + (v & 3) > pos) sacc[mb][v] = -INFINITY;
+          if (32 * mb + 8 * (v >> 2) + (v & 3) > lim) sacc[mb][v] = -INFINITY;
     }
     // Probabilities against the running max m without a max pass: p =
     // exp2(s c - m), rounded to bf16 (the PV operand), and this lane's sum of
@@ -386,10 +389,13 @@ __global__ void __launch_bounds__(64 * kWaves, 8 / kWaves) extend_kernel(AttnArg
       const float mn = fmaxf(m, tmax);
       alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mn);
       m = mn;
+      // the first tile of an item (every row's m was -inf) has nothing to rescale
+      if (__ballot(alpha != 0.f) != 0) {
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+        for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[nb][v] *= alpha;
+          for (int v = 0; v < 16; ++v) oacc[nb][v] *= alpha;
+      }
       make_p(m == -INFINITY ? 0.f : -m);
     }
 
